@@ -6,6 +6,8 @@ CPU-baseline leg of ``bench.py`` do.  The arithmetic lives in plain C
 (``trimul_oracle.c``, fp64 loops); this module only compiles it with gcc and
 marshals numpy arrays through ctypes.
 """
-from .oracle import build, lib_path, max_threads, trimul_full, trimul_grid, gather_grid
+from .oracle import (build, lib_path, max_threads, trimul_full, trimul_grid, gather_grid,
+                     output_stage)
 
-__all__ = ["build", "lib_path", "max_threads", "trimul_full", "trimul_grid", "gather_grid"]
+__all__ = ["build", "lib_path", "max_threads", "trimul_full", "trimul_grid", "gather_grid",
+           "output_stage"]

@@ -53,6 +53,9 @@ def _load():
         lib.orc_trimul_grid.argtypes = [ci, ci, ci, ci, ci, fp, fp, fp, fp, fp, fp, fp, fp, fp, fp,
                                         fp, fp, fp, ctypes.c_double, dp, dp, dp]
         lib.orc_trimul_grid.restype = ci
+        lib.orc_output_stage.argtypes = [ctypes.c_int64, ci, ci, fp, fp, fp, fp, fp, fp, fp, fp,
+                                         ctypes.c_double, dp]
+        lib.orc_output_stage.restype = ci
         lib.orc_max_threads.argtypes = []
         lib.orc_max_threads.restype = ci
         _lib = lib
@@ -219,3 +222,25 @@ def trimul_grid(N, w, zA, mA, zB, mB, zG, want_o=False, want_times=False):
     if want_times:
         res.append(t)
     return res[0] if len(res) == 1 else tuple(res)
+
+
+def output_stage(z, o, w):
+    """Output stage alone for pairs: z [..., D] and o [..., C] (same leading shape).
+
+    Returns out [..., D] float64.
+    """
+    lib = _load()
+    z = _f32(_to_np(z))
+    o = _f32(_to_np(o))
+    D, C = z.shape[-1], o.shape[-1]
+    lead = z.shape[:-1]
+    assert o.shape[:-1] == lead
+    P = int(np.prod(lead)) if len(lead) else 1
+    W = _weights(w, D, C)
+    out = np.empty(lead + (D,), np.float64)
+    Wp = [_fp(t) for t in W]
+    rc = lib.orc_output_stage(P, D, C, _fp(z), _fp(o), Wp[0], Wp[1], Wp[4], Wp[5], Wp[6], Wp[7],
+                              float(w.eps), _dp(out))
+    if rc != 0:
+        raise RuntimeError("orc_output_stage failed (%d)" % rc)
+    return out

@@ -83,12 +83,16 @@ static void project_pair(const orc_weights *w, const float *z_pair, double m,
     for (int d = 0; d < D; ++d) zd[d] = (double)z_pair[d];
     layer_norm(zd, D, w->ln_in_w, w->ln_in_b, w->eps, x);
     for (int c = 0; c < C; ++c) {
-        double pa = dot_row(w->p_in + (size_t)c * D, x, D);
-        double ga = dot_row(w->g_in + (size_t)c * D, x, D);
-        double pb = dot_row(w->p_in + (size_t)(C + c) * D, x, D);
-        double gb = dot_row(w->g_in + (size_t)(C + c) * D, x, D);
-        if (a) a[c] = m * pa * sigm(ga);
-        if (b) b[c] = m * pb * sigm(gb);
+        if (a) {
+            double pa = dot_row(w->p_in + (size_t)c * D, x, D);
+            double ga = dot_row(w->g_in + (size_t)c * D, x, D);
+            a[c] = m * pa * sigm(ga);
+        }
+        if (b) {
+            double pb = dot_row(w->p_in + (size_t)(C + c) * D, x, D);
+            double gb = dot_row(w->g_in + (size_t)(C + c) * D, x, D);
+            b[c] = m * pb * sigm(gb);
+        }
     }
 }
 
@@ -270,5 +274,31 @@ int orc_trimul_grid(int N, int D, int C, int ni, int nj,
     if (o_dump) memcpy(o_dump, o, sizeof(double) * (size_t)ni * nj * C);
     if (t_stage) { t_stage[0] = t1 - t0; t_stage[1] = t2 - t1; t_stage[2] = t3 - t2; }
     free(ar); free(br); free(o);
+    return 0;
+}
+
+/*
+ * Output stage alone: for P pairs with given o [P][C] and z [P][D] (both float
+ * inputs widened to double), out[p] = (p_out LayerNorm_out(o_p)) *
+ * sigm(g_out LayerNorm_in(z_p)).  Used to check the output kernel by itself.
+ */
+int orc_output_stage(int64_t P, int D, int C, const float *z, const float *o,
+                     const float *ln_in_w, const float *ln_in_b,
+                     const float *ln_out_w, const float *ln_out_b,
+                     const float *p_out, const float *g_out, double eps, double *out)
+{
+    if (P < 0 || check_dims(D, C)) return 1;
+    orc_weights w = {ln_in_w, ln_in_b, NULL, NULL, ln_out_w, ln_out_b, p_out, g_out, eps, D, C};
+    #pragma omp parallel
+    {
+        double xs[256], zd[256], od[256];
+        #pragma omp for schedule(static)
+        for (int64_t p = 0; p < P; ++p) {
+            for (int d = 0; d < D; ++d) zd[d] = (double)z[(size_t)p * D + d];
+            for (int c = 0; c < C; ++c) od[c] = (double)o[(size_t)p * C + c];
+            layer_norm(zd, D, w.ln_in_w, w.ln_in_b, w.eps, xs);
+            output_pair(&w, od, xs, out + (size_t)p * D);
+        }
+    }
     return 0;
 }

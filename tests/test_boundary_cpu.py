@@ -1,0 +1,144 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every entry point the headers declare, and rejects bad arguments with the
+documented status codes before touching a device."""
+import ctypes
+import glob
+import os
+import re
+
+import numpy as np
+import pytest
+
+from triangle_multiplication_amd import binding as tb
+from triangle_multiplication_amd import inputs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names.update(re.findall(r"\b(trimul_[a-z_]+)\s*\(", text))
+    return sorted(names)
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared_functions()
+    assert "trimul_fwd" in names and "trimul_create" in names and "trimul_destroy" in names
+    lib = ctypes.CDLL(tb.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), "libtrimul does not export " + n
+    assert set(names) == set(tb.EXPORTED)
+
+
+def test_status_strings():
+    for code, name in enumerate(["TRIMUL_OK", "TRIMUL_ERR_INVALID_ARG", "TRIMUL_ERR_UNSUPPORTED",
+                                 "TRIMUL_ERR_ARCH", "TRIMUL_ERR_WORKSPACE", "TRIMUL_ERR_HIP"]):
+        assert tb.trimul_status_string(code) == name
+    assert tb.trimul_status_string(99) == "TRIMUL_ERR_UNKNOWN"
+
+
+@pytest.mark.parametrize("name", ["gfx950", "gfx950:sramecc+:xnack-", "gfx950:xnack+"])
+def test_arch_gate_accepts_gfx950(name):
+    tb.trimul_check_arch(name)
+
+
+@pytest.mark.parametrize("name", ["gfx942", "gfx942:sramecc+:xnack-", "gfx90a", "gfx9500", "gfx95", ""])
+def test_arch_gate_refuses_others(name):
+    with pytest.raises(tb.TriMulError) as e:
+        tb.trimul_check_arch(name)
+    assert e.value.status == tb.TRIMUL_ERR_ARCH
+    assert "requires gfx950" in str(e.value) and ("got " + name) in str(e.value)
+
+
+def test_arch_gate_null():
+    with pytest.raises(tb.TriMulError) as e:
+        tb.trimul_check_arch(None)
+    assert e.value.status == tb.TRIMUL_ERR_INVALID_ARG
+
+
+def test_workspace_query_sizes():
+    # a, b and o, each [B][C][N][N], 256-byte aligned
+    assert tb.trimul_workspace_query(256, 256, "bf16", 1, 4096) == 3 * 256 * 4096 * 4096 * 2
+    assert tb.trimul_workspace_query(32, 32, "fp32", 1, 64) == 3 * 32 * 64 * 64 * 4
+    n = tb.trimul_workspace_query(32, 64, "bf16", 3, 8)
+    slab = 3 * 64 * 8 * 8 * 2
+    assert n == 3 * ((slab + 255) // 256 * 256)
+    assert tb.trimul_workspace_query(128, 128, "bf16", 1, 8192) == 3 * 128 * 8192 ** 2 * 2
+
+
+@pytest.mark.parametrize("D,C", [(48, 32), (32, 0), (288, 32), (32, 300), (16, 16)])
+def test_workspace_query_unsupported_widths(D, C):
+    with pytest.raises(tb.TriMulError) as e:
+        tb.trimul_workspace_query(D, C, "bf16", 1, 64)
+    assert e.value.status == tb.TRIMUL_ERR_UNSUPPORTED
+
+
+def test_workspace_query_bad_dtype_and_sizes():
+    with pytest.raises(tb.TriMulError) as e:
+        tb.trimul_workspace_query(32, 32, 7, 1, 64)
+    assert e.value.status == tb.TRIMUL_ERR_INVALID_ARG
+    with pytest.raises(tb.TriMulError) as e:
+        tb.trimul_workspace_query(32, 32, "bf16", 0, 64)
+    assert e.value.status == tb.TRIMUL_ERR_INVALID_ARG
+
+
+def test_create_rejects_bad_widths_before_any_device_call():
+    w = inputs.make_weights(48, 32)
+    with pytest.raises(tb.TriMulError) as e:
+        tb.trimul_create(w)
+    assert e.value.status == tb.TRIMUL_ERR_UNSUPPORTED and "D=48" in str(e.value)
+
+
+def test_create_rejects_bad_eps():
+    w = inputs.make_weights(32, 32).replace(eps=0.0)
+    with pytest.raises(tb.TriMulError) as e:
+        tb.trimul_create(w)
+    assert e.value.status == tb.TRIMUL_ERR_INVALID_ARG and "eps" in str(e.value)
+
+
+def test_create_null_weight_pointer():
+    lib = ctypes.CDLL(tb.LIB_PATH)
+    lib.trimul_create.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                  ctypes.POINTER(tb.trimul_weights), ctypes.POINTER(ctypes.c_void_p)]
+    w = tb.trimul_weights()  # all NULL
+    w.eps = 1e-5
+    h = ctypes.c_void_p()
+    assert lib.trimul_create(32, 32, 0, ctypes.byref(w), ctypes.byref(h)) == tb.TRIMUL_ERR_INVALID_ARG
+    assert "norm_in_weight" in tb.trimul_last_error()
+    assert lib.trimul_create(32, 32, 0, None, ctypes.byref(h)) == tb.TRIMUL_ERR_INVALID_ARG
+    assert lib.trimul_create(32, 32, 0, ctypes.byref(w), None) == tb.TRIMUL_ERR_INVALID_ARG
+
+
+def test_fwd_null_handle():
+    lib = ctypes.CDLL(tb.LIB_PATH)
+    lib.trimul_fwd.argtypes = tb._lib.trimul_fwd.argtypes
+    rc = lib.trimul_fwd(None, None, None, 1, 64, 0, None, None, 0, None)
+    assert rc == tb.TRIMUL_ERR_INVALID_ARG and "handle" in tb.trimul_last_error()
+
+
+def test_destroy_accepts_null():
+    tb.trimul_destroy(None)
+
+
+def test_create_without_device_reports_hip_error():
+    """On a host with no GPU the first device query fails cleanly (no crash)."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    w = inputs.make_weights(32, 32)
+    with pytest.raises(tb.TriMulError) as e:
+        tb.trimul_create(w)
+    assert e.value.status == tb.TRIMUL_ERR_HIP
+
+
+def test_product_path_does_not_reference_the_oracle():
+    """Nothing under the package may import or load the oracle."""
+    pkg = os.path.join(ROOT, "triangle_multiplication_amd")
+    for f in glob.glob(os.path.join(pkg, "**", "*"), recursive=True):
+        if os.path.isfile(f) and f.endswith((".py", ".cpp", ".hip", ".hpp", ".h")):
+            text = open(f).read()
+            assert "import oracle" not in text and "from oracle" not in text, f
+            assert "orc_" not in text and "liborc" not in text, f

@@ -1,0 +1,324 @@
+"""GPU parity of libtrimul against the fp64 oracle, through the C ABI.
+
+Tolerances (normalised max error, max|got - ref| / max|ref|): 1e-4 for the
+fp32 path, 2e-2 for bf16 storage with fp32 statistics and accumulation.
+Small shapes are compared element by element in full; N >= 1024 on a seeded
+64 x 64 grid of (i, j) outputs per batch element, which the oracle computes
+one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from triangle_multiplication_amd import inputs
+
+from _helpers import oracle_check, rel_err, say, workload_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 2e-2, "fp32": 1e-4}
+
+
+@pytest.fixture(scope="module")
+def tb():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from triangle_multiplication_amd import binding
+    return binding
+
+
+@pytest.fixture(autouse=True)
+def _free_memory():
+    yield
+    if torch.cuda.is_available():
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
+
+def _layer(tb, w, dtype):
+    return tb.TriMul(w, dtype)
+
+
+def _exact_contract_reference(a, b, rows=None, chans=None):
+    """RNE-rounded exact integer sums sum_k a[c,i,k] b[c,j,k] in float64 on the device."""
+    A = a if chans is None else a[:, chans]
+    Bm = b if chans is None else b[:, chans]
+    if rows is not None:
+        A = A[:, :, rows]
+    ref = torch.matmul(A.double(), Bm.double().transpose(-1, -2).contiguous())
+    return ref
+
+
+# ----------------------------------------------------------------------------
+# Contraction kernel alone: exact on small integers (bitwise)
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("B,C,N", [(1, 32, 8), (2, 32, 200), (1, 64, 136), (1, 32, 384)])
+def test_contract_exact_integers(tb, dtype, B, C, N):
+    say("contract exact", dtype, B, C, N)
+    w = inputs.make_weights(C, C, dtype)
+    layer = _layer(tb, w, dtype)
+    g = torch.Generator(device="cuda").manual_seed(7)
+    tdt = inputs.TORCH_DTYPES[dtype]
+    a = torch.randint(-3, 4, (B, C, N, N), generator=g, device="cuda").to(tdt)
+    b = torch.randint(-3, 4, (B, C, N, N), generator=g, device="cuda").to(tdt)
+    o = layer.contract(a, b)
+    ref = _exact_contract_reference(a, b).to(tdt)
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref)
+
+
+@pytest.mark.parametrize("C,N", [(256, 4096), (128, 8192)])
+def test_contract_exact_integers_full_size(tb, C, N):
+    """Full workload shapes (every tile and the whole K loop), checked on sampled rows."""
+    say("contract exact full size", C, N)
+    w = inputs.make_weights(C, C, "bf16")
+    layer = _layer(tb, w, "bf16")
+    g = torch.Generator(device="cuda").manual_seed(8)
+    a = torch.randint(-3, 4, (1, C, N, N), generator=g, device="cuda", dtype=torch.int8).to(torch.bfloat16)
+    b = torch.randint(-3, 4, (1, C, N, N), generator=g, device="cuda", dtype=torch.int8).to(torch.bfloat16)
+    o = layer.contract(a, b)
+    I, _ = inputs.sample_grid(N, 64)
+    rows = torch.as_tensor(I, device="cuda")
+    chans = torch.as_tensor([0, 1, C // 2 + 3, C - 1], device="cuda")
+    ref = _exact_contract_reference(a, b, rows=rows, chans=chans).to(torch.bfloat16)
+    got = o[:, chans][:, :, rows]
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
+
+
+# ----------------------------------------------------------------------------
+# Projection kernel alone against the oracle's a and b
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("direction", ["outgoing", "incoming"])
+@pytest.mark.parametrize("B,N,D,C", [(2, 40, 64, 64), (1, 72, 128, 32), (1, 16, 96, 160)])
+def test_project_stage(tb, dtype, direction, B, N, D, C):
+    say("project stage", dtype, direction, B, N, D, C)
+    w = inputs.make_weights(D, C, dtype, random_ln=True)
+    z = inputs.make_z(B, N, D, dtype)
+    tm = np.ones(N, np.float32)
+    tm[N - 5:] = 0
+    tm[1] = 0
+    mask = inputs.pair_mask(tm, B, dtype)
+    ref = oracle.trimul_full(z.float().numpy(), mask.float().numpy(), w, direction, dumps=True)
+    layer = _layer(tb, w, dtype)
+    a, b = layer.project(z.cuda(), mask.cuda(), direction)
+    a, b = a.float().cpu().numpy(), b.float().cpu().numpy()
+    ra, rb = ref["a"], ref["b"]  # [B, N, N, C] pair layout
+    if direction == "outgoing":
+        ea, eb = ra.transpose(0, 3, 1, 2), rb.transpose(0, 3, 1, 2)
+    else:
+        ea, eb = ra.transpose(0, 3, 2, 1), rb.transpose(0, 3, 2, 1)
+    assert rel_err(a, ea) <= TOL[dtype]
+    assert rel_err(b, eb) <= TOL[dtype]
+    # masked pairs give exact zeros
+    dead = np.nonzero(tm == 0)[0]
+    if direction == "outgoing":
+        assert (a[:, :, dead, :] == 0).all() and (a[:, :, :, dead] == 0).all()
+    else:
+        assert (a[:, :, :, dead] == 0).all() and (a[:, :, dead, :] == 0).all()
+
+
+# ----------------------------------------------------------------------------
+# Output kernel alone against the oracle's output stage
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("B,N,D,C", [(1, 24, 64, 64), (2, 40, 32, 96), (1, 16, 256, 256), (1, 8, 160, 224)])
+def test_output_stage(tb, dtype, B, N, D, C):
+    say("output stage", dtype, B, N, D, C)
+    w = inputs.make_weights(D, C, dtype, random_ln=True)
+    z = inputs.make_z(B, N, D, dtype)
+    g = torch.Generator("cpu").manual_seed(9)
+    o = (torch.randn((B, C, N, N), generator=g) * 3.0 + 0.5).to(inputs.TORCH_DTYPES[dtype])
+    ref = oracle.output_stage(z.float().numpy(), o.float().permute(0, 2, 3, 1).numpy(), w)
+    layer = _layer(tb, w, dtype)
+    out = layer.output(z.cuda(), o.cuda())
+    assert rel_err(out.float().cpu().numpy(), ref) <= TOL[dtype]
+
+
+# ----------------------------------------------------------------------------
+# End to end
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("direction", ["outgoing", "incoming"])
+@pytest.mark.parametrize("B,N,D,C,masked", [(1, 8, 32, 32, False), (3, 24, 64, 96, True),
+                                            (1, 72, 128, 128, True), (2, 136, 32, 64, False),
+                                            (1, 40, 256, 256, True), (1, 48, 160, 32, True)])
+def test_fwd_small_shapes(tb, dtype, direction, B, N, D, C, masked):
+    say("fwd small", dtype, direction, B, N, D, C, masked)
+    w = inputs.make_weights(D, C, dtype, random_ln=True)
+    z = inputs.make_z(B, N, D, dtype)
+    mask = None
+    if masked:
+        tm = np.ones(N, np.float32)
+        tm[N - max(1, N // 10):] = 0
+        tm[N // 3] = 0
+        mask = inputs.pair_mask(tm, B, dtype)
+    layer = _layer(tb, w, dtype)
+    out = layer.forward(z.cuda(), None if mask is None else mask.cuda(), direction)
+    err = oracle_check(z, mask, w, direction, out, full=True)
+    say("  err", err)
+    assert err <= TOL[dtype]
+
+
+WL = inputs.WORKLOADS
+
+
+def _run_workload(tb, name, direction):
+    wl = WL[name]
+    say("workload", name, direction)
+    z, mask, w = workload_inputs(wl)
+    layer = _layer(tb, w, wl.dtype)
+    out = layer.forward(z, mask, direction)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    err = oracle_check(z, mask, w, direction, out, full=(wl.check == "full"),
+                       extra=wl.sample_extra())
+    say("  err", err)
+    assert err <= wl.tol
+    return z, mask, w, layer, out
+
+
+def test_workload_out_fp32_b1_n64_d32(tb):
+    _run_workload(tb, "out_fp32_b1_n64_d32", "outgoing")
+
+
+@pytest.mark.parametrize("direction", ["outgoing", "incoming"])
+def test_workload_outin_bf16_b1_n384_d128_tailmask(tb, direction):
+    z, mask, w, layer, out = _run_workload(tb, "outin_bf16_b1_n384_d128_tailmask", direction)
+    # every pair touching a padded token: o = 0, so out = p_out(beta_out) * gate = 0 with beta = 0
+    n_pad = 38
+    assert (out[0, -n_pad:, :] == 0).all() and (out[0, :, -n_pad:] == 0).all()
+
+
+@pytest.mark.parametrize("direction", ["outgoing", "incoming"])
+def test_workload_outin_bf16_b2_n1024_d128(tb, direction):
+    _run_workload(tb, "outin_bf16_b2_n1024_d128", direction)
+
+
+# ----------------------------------------------------------------------------
+# Invariants on the GPU
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("direction", ["outgoing", "incoming"])
+def test_mask_garbage_invariance_bitwise(tb, direction):
+    wl = WL["outin_bf16_b1_n384_d128_tailmask"]
+    say("mask garbage", direction)
+    z, mask, w = workload_inputs(wl)
+    layer = _layer(tb, w, "bf16")
+    out1 = layer.forward(z, mask, direction)
+    g = torch.Generator(device="cuda").manual_seed(11)
+    junk = (torch.randn(z.shape, generator=g, device="cuda") * 40.0).to(z.dtype)
+    z2 = torch.where((mask == 0)[..., None], junk, z)
+    out2 = layer.forward(z2, mask, direction)
+    keep = mask[0] != 0
+    assert torch.equal(out1[0][keep], out2[0][keep])
+
+
+def test_determinism_bitwise(tb):
+    wl = WL["outin_bf16_b1_n384_d128_tailmask"]
+    z, mask, w = workload_inputs(wl)
+    layer = _layer(tb, w, "bf16")
+    o1 = layer.forward(z, mask, "incoming")
+    o2 = layer.forward(z, mask, "incoming")
+    assert torch.equal(o1, o2)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_transpose_identity_bitwise(tb, dtype):
+    """With g_out = 0 (gate 1/2 everywhere), incoming on (z, m) equals outgoing on the transposes."""
+    B, N, D, C = 2, 72, 64, 64
+    w = inputs.make_weights(D, C, dtype, random_ln=True)
+    w = w.replace(g_out=np.zeros_like(w.g_out))
+    z = inputs.make_z(B, N, D, dtype).cuda()
+    tm = np.ones(N, np.float32)
+    tm[5] = 0
+    mask = inputs.pair_mask(tm, B, dtype).cuda()
+    mask[:, 3, :] = 0  # non-symmetric
+    layer = _layer(tb, w, dtype)
+    o_in = layer.forward(z, mask, "incoming")
+    o_out = layer.forward(z.transpose(1, 2).contiguous(), mask.transpose(1, 2).contiguous(), "outgoing")
+    assert torch.equal(o_in, o_out)
+
+
+def test_guard_bands_untouched(tb):
+    B, N, D, C = 1, 72, 64, 64
+    w = inputs.make_weights(D, C, "bf16")
+    layer = _layer(tb, w, "bf16")
+    z = inputs.make_z(B, N, D, "bf16").cuda()
+    n_out = B * N * N * D
+    pad = 4096
+    big = torch.full((n_out + 2 * pad,), 1234.0, dtype=torch.bfloat16, device="cuda")
+    out = big[pad:pad + n_out].view(B, N, N, D)
+    ws_need = tb.trimul_workspace_size(layer.h, B, N)
+    wbig = torch.full((ws_need + 2 * pad,), 0x5A, dtype=torch.uint8, device="cuda")
+    ws = wbig[pad:pad + ws_need]
+    tb.trimul_fwd(layer.h, z, None, "outgoing", out, ws)
+    torch.cuda.synchronize()
+    assert (big[:pad] == 1234.0).all() and (big[pad + n_out:] == 1234.0).all()
+    assert (wbig[:pad] == 0x5A).all() and (wbig[pad + ws_need:] == 0x5A).all()
+
+
+def test_error_paths_on_device(tb):
+    B, N, D, C = 1, 16, 32, 32
+    w = inputs.make_weights(D, C, "bf16")
+    layer = _layer(tb, w, "bf16")
+    z = inputs.make_z(B, N, D, "bf16").cuda()
+    out = torch.empty_like(z)
+    need = tb.trimul_workspace_size(layer.h, B, N)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    with pytest.raises(tb.TriMulError) as e:
+        tb.trimul_fwd(layer.h, z, None, "outgoing", out, ws[: need - 256])
+    assert e.value.status == tb.TRIMUL_ERR_WORKSPACE
+    with pytest.raises(tb.TriMulError) as e:
+        tb.trimul_fwd(layer.h, z, None, "outgoing", z, ws)
+    assert e.value.status == tb.TRIMUL_ERR_INVALID_ARG and "overlaps" in str(e.value)
+    zbig = torch.empty(z.numel() + 8, dtype=z.dtype, device="cuda")
+    zmis = zbig[1:1 + z.numel()].view(z.shape)
+    with pytest.raises(tb.TriMulError) as e:
+        tb.trimul_fwd(layer.h, zmis, None, "outgoing", out, ws)
+    assert e.value.status == tb.TRIMUL_ERR_INVALID_ARG and "aligned" in str(e.value)
+    z12 = torch.zeros((1, 12, 12, D), dtype=z.dtype, device="cuda")
+    with pytest.raises(tb.TriMulError) as e:
+        tb.trimul_fwd(layer.h, z12, None, "outgoing", torch.empty_like(z12), ws)
+    assert e.value.status == tb.TRIMUL_ERR_INVALID_ARG and "multiple of 8" in str(e.value)
+    with pytest.raises(tb.TriMulError) as e:
+        tb.trimul_fwd(layer.h, z, None, 5, out, ws)
+    assert e.value.status == tb.TRIMUL_ERR_INVALID_ARG
+
+
+def test_arch_gate_accepts_this_device(tb):
+    name = torch.cuda.get_device_properties(0).gcnArchName
+    tb.trimul_check_arch(name)
+
+
+# ----------------------------------------------------------------------------
+# Full-size workloads (last: they hold tens of GB)
+# ----------------------------------------------------------------------------
+def test_constant_z_full_size(tb):
+    """z equal at every pair: every output row is the same vector, equal to the oracle's."""
+    B, N, D, C = 1, 4096, 256, 256
+    say("constant z full size")
+    w = inputs.make_weights(D, C, "bf16", random_ln=True)
+    v = inputs.make_z(1, 1, D, "bf16", seed=5)[0, 0, 0]
+    z = v.cuda().expand(B, N, N, D).contiguous()
+    layer = _layer(tb, w, "bf16")
+    out = layer.forward(z, None, "outgoing")
+    torch.cuda.synchronize()
+    assert (out == out[0, 0, 0]).all()
+    vz = v.float().numpy()[None, None]
+    zA = np.broadcast_to(vz, (1, N, D))
+    ref = oracle.trimul_grid(N, w, zA, None, zA, None, vz)
+    assert rel_err(out[0, 0, 0].float().cpu().numpy(), ref[0, 0]) <= 2e-2
+    del out, z
+
+
+def test_workload_out_bf16_b1_n4096_d256(tb):
+    _run_workload(tb, "out_bf16_b1_n4096_d256", "outgoing")
+
+
+def test_workload_in_bf16_b1_n8192_d128_chains(tb):
+    z, mask, w, layer, out = _run_workload(tb, "in_bf16_b1_n8192_d128_chains", "incoming")
+    # padded tail rows and columns are exactly zero (beta_out = 0)
+    assert (out[0, 7800:, :: 97] == 0).all() and (out[0, ::97, 7800:] == 0).all()

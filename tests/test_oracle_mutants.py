@@ -14,7 +14,8 @@ MUTANTS = {
     "eps_outside_sqrt": ("1.0 / sqrt(var + eps)", "1.0 / (sqrt(var) + eps)"),
     "dropped_beta": ("* (double)gamma[d] + (double)beta[d]", "* (double)gamma[d]"),
     "sigmoid_sign": ("1.0 / (1.0 + exp(-t))", "1.0 / (1.0 + exp(t))"),
-    "a_gated_by_b_gate": ("a[c] = m * pa * sigm(ga)", "a[c] = m * pa * sigm(gb)"),
+    "a_gated_by_b_gate": ("double ga = dot_row(w->g_in + (size_t)c * D, x, D);",
+                          "double ga = dot_row(w->g_in + (size_t)(C + c) * D, x, D);"),
     "b_unmasked": ("b[c] = m * pb * sigm(gb)", "b[c] = pb * sigm(gb)"),
     "incoming_as_outgoing": ("ta = a + ((size_t)k * N + i) * C;", "ta = a + ((size_t)i * N + k) * C;"),
     "outgoing_transposed_b": ("tb = b + ((size_t)j * N + k) * C;", "tb = b + ((size_t)k * N + j) * C;"),

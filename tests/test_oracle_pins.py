@@ -294,3 +294,16 @@ def test_rejects_bad_arguments():
         oracle.trimul_full(_rand_z(1, 3, 16), None, w, "sideways")
     with pytest.raises(ValueError):
         oracle.trimul_full(_rand_z(1, 3, 16), np.ones((1, 3, 4), np.float32), w, 0)
+
+
+def test_output_stage_matches_full_mode():
+    """The stand-alone output stage reproduces full mode from the same o (values exact in float)."""
+    B, N, D, C = 1, 5, 32, 16
+    z = _rand_z(B, N, D, seed=22)
+    w = _weights(D, C, random_ln=True)
+    r = oracle.trimul_full(z, None, w, "outgoing", dumps=True)
+    o32 = r["o"].astype(np.float32)
+    out = oracle.output_stage(z, o32, w)
+    ref = _ln_lib(o32.astype(np.float64), w.ln_out_w, w.ln_out_b, w.eps)
+    ref = (ref @ w.p_out.astype(np.float64).T) * expit(r["x"] @ w.g_out.astype(np.float64).T)
+    np.testing.assert_allclose(out, ref, rtol=1e-11, atol=1e-12)

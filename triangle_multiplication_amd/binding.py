@@ -1,0 +1,235 @@
+"""Thin ctypes binding of libtrimul (``include/trimul.h``).
+
+Argument marshalling only: torch tensors become device pointers, the current
+torch stream becomes the hipStream_t, and status codes become exceptions.
+Every step of the computation runs in the library's HIP kernels.  Importing
+this module loads ``libtrimul.so`` and raises if it has not been built; there
+is no fallback.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtrimul.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError("libtrimul.so is not built (expected at %s); run "
+                      "`python -c 'import __graft_entry__ as g; g.build()'`" % LIB_PATH)
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+TRIMUL_OK, TRIMUL_ERR_INVALID_ARG, TRIMUL_ERR_UNSUPPORTED, TRIMUL_ERR_ARCH, \
+    TRIMUL_ERR_WORKSPACE, TRIMUL_ERR_HIP = range(6)
+TRIMUL_BF16, TRIMUL_FP32 = 0, 1
+TRIMUL_OUTGOING, TRIMUL_INCOMING = 0, 1
+DTYPES = {"bf16": TRIMUL_BF16, "fp32": TRIMUL_FP32}
+DIRECTIONS = {"outgoing": TRIMUL_OUTGOING, "incoming": TRIMUL_INCOMING,
+              0: TRIMUL_OUTGOING, 1: TRIMUL_INCOMING}
+
+EXPORTED = ["trimul_create", "trimul_destroy", "trimul_workspace_size", "trimul_workspace_query",
+            "trimul_fwd", "trimul_check_arch", "trimul_status_string", "trimul_last_error",
+            "trimul_internal_project", "trimul_internal_contract", "trimul_internal_output"]
+
+
+class trimul_weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.POINTER(ctypes.c_float)) for n in
+                ("norm_in_weight", "norm_in_bias", "p_in", "g_in", "norm_out_weight",
+                 "norm_out_bias", "p_out", "g_out")] + [("eps", ctypes.c_float)]
+
+
+_vp, _ci, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+_lib.trimul_create.argtypes = [_ci, _ci, _ci, ctypes.POINTER(trimul_weights), ctypes.POINTER(_vp)]
+_lib.trimul_create.restype = _ci
+_lib.trimul_destroy.argtypes = [_vp]
+_lib.trimul_destroy.restype = None
+_lib.trimul_workspace_size.argtypes = [_vp, _ci, _ci, ctypes.POINTER(_sz)]
+_lib.trimul_workspace_size.restype = _ci
+_lib.trimul_workspace_query.argtypes = [_ci, _ci, _ci, _ci, _ci, ctypes.POINTER(_sz)]
+_lib.trimul_workspace_query.restype = _ci
+_lib.trimul_fwd.argtypes = [_vp, _vp, _vp, _ci, _ci, _ci, _vp, _vp, _sz, _vp]
+_lib.trimul_fwd.restype = _ci
+_lib.trimul_check_arch.argtypes = [ctypes.c_char_p]
+_lib.trimul_check_arch.restype = _ci
+_lib.trimul_status_string.argtypes = [_ci]
+_lib.trimul_status_string.restype = ctypes.c_char_p
+_lib.trimul_last_error.argtypes = []
+_lib.trimul_last_error.restype = ctypes.c_char_p
+_lib.trimul_internal_project.argtypes = [_vp, _vp, _vp, _ci, _ci, _ci, _vp, _vp, _vp]
+_lib.trimul_internal_project.restype = _ci
+_lib.trimul_internal_contract.argtypes = [_vp, _vp, _vp, _ci, _ci, _vp, _vp]
+_lib.trimul_internal_contract.restype = _ci
+_lib.trimul_internal_output.argtypes = [_vp, _vp, _vp, _ci, _ci, _vp, _vp]
+_lib.trimul_internal_output.restype = _ci
+
+
+class TriMulError(RuntimeError):
+    def __init__(self, status, message):
+        self.status = status
+        super().__init__("%s: %s" % (trimul_status_string(status), message))
+
+
+def trimul_status_string(status):
+    return _lib.trimul_status_string(int(status)).decode()
+
+
+def trimul_last_error():
+    return _lib.trimul_last_error().decode()
+
+
+def _check(status):
+    if status != TRIMUL_OK:
+        raise TriMulError(status, trimul_last_error())
+
+
+def trimul_check_arch(name):
+    """Raise TriMulError unless ``name`` is a gfx950 architecture string."""
+    _check(_lib.trimul_check_arch(name.encode() if name is not None else None))
+
+
+def trimul_workspace_query(D, C, dtype, B, N):
+    n = _sz(0)
+    _check(_lib.trimul_workspace_query(D, C, DTYPES.get(dtype, dtype), B, N, ctypes.byref(n)))
+    return n.value
+
+
+def _f32p(a, keep):
+    a = np.ascontiguousarray(np.asarray(a, np.float32))
+    keep.append(a)
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+
+
+def trimul_create(weights, dtype="bf16"):
+    """Create a handle from host fp32 weights (a TriMulWeights-like object)."""
+    keep = []
+    w = trimul_weights(_f32p(weights.ln_in_w, keep), _f32p(weights.ln_in_b, keep),
+                       _f32p(weights.p_in, keep), _f32p(weights.g_in, keep),
+                       _f32p(weights.ln_out_w, keep), _f32p(weights.ln_out_b, keep),
+                       _f32p(weights.p_out, keep), _f32p(weights.g_out, keep),
+                       float(weights.eps))
+    D, C = int(np.asarray(weights.ln_in_w).shape[0]), int(np.asarray(weights.ln_out_w).shape[0])
+    h = _vp()
+    _check(_lib.trimul_create(D, C, DTYPES.get(dtype, dtype), ctypes.byref(w), ctypes.byref(h)))
+    return h
+
+
+def trimul_destroy(h):
+    _lib.trimul_destroy(h)
+
+
+def trimul_workspace_size(h, B, N):
+    n = _sz(0)
+    _check(_lib.trimul_workspace_size(h, B, N, ctypes.byref(n)))
+    return n.value
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def trimul_fwd(h, z, mask, direction, out, workspace, stream=None):
+    """Enqueue the forward pass on ``stream`` (default: torch's current stream)."""
+    B, N = int(z.shape[0]), int(z.shape[1])
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib.trimul_fwd(h, _ptr(z), _ptr(mask), B, N, DIRECTIONS[direction], _ptr(out),
+                           _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def trimul_internal_project(h, z, mask, direction, a_cm, b_cm, stream=None):
+    B, N = int(z.shape[0]), int(z.shape[1])
+    _check(_lib.trimul_internal_project(h, _ptr(z), _ptr(mask), B, N, DIRECTIONS[direction],
+                                        _ptr(a_cm), _ptr(b_cm), _stream(stream)))
+
+
+def trimul_internal_contract(h, a_cm, b_cm, o, stream=None):
+    B, N = int(a_cm.shape[0]), int(a_cm.shape[2])
+    _check(_lib.trimul_internal_contract(h, _ptr(a_cm), _ptr(b_cm), B, N, _ptr(o),
+                                         _stream(stream)))
+
+
+def trimul_internal_output(h, z, o, out, stream=None):
+    B, N = int(z.shape[0]), int(z.shape[1])
+    _check(_lib.trimul_internal_output(h, _ptr(z), _ptr(o), B, N, _ptr(out), _stream(stream)))
+
+
+class TriMul:
+    """One layer on the current device: owns a handle and a cached workspace.
+
+    ``forward(z, mask, direction)`` returns a new [B, N, N, D] tensor (or fills
+    ``out``).  Tensors must be contiguous, on the device the handle was created
+    on, in the handle's dtype.
+    """
+
+    def __init__(self, weights, dtype="bf16"):
+        import torch
+        self.dtype = dtype
+        self.tdtype = {"bf16": torch.bfloat16, "fp32": torch.float32}[dtype]
+        self.D = int(np.asarray(weights.ln_in_w).shape[0])
+        self.C = int(np.asarray(weights.ln_out_w).shape[0])
+        self.h = trimul_create(weights, dtype)
+        self._ws = None
+
+    def workspace(self, B, N, device):
+        import torch
+        need = trimul_workspace_size(self.h, B, N)
+        if self._ws is None or self._ws.numel() < need or self._ws.device != device:
+            self._ws = None
+            self._ws = torch.empty(need, dtype=torch.uint8, device=device)
+        return self._ws
+
+    def _check_tensor(self, t, name, shape):
+        if t.dtype != self.tdtype or not t.is_contiguous() or not t.is_cuda or tuple(t.shape) != shape:
+            raise ValueError("%s must be a contiguous %s device tensor of shape %s; got %s %s %s"
+                             % (name, self.tdtype, shape, t.dtype, tuple(t.shape), t.device))
+
+    def forward(self, z, mask=None, direction="outgoing", out=None, stream=None):
+        import torch
+        B, N = int(z.shape[0]), int(z.shape[1])
+        self._check_tensor(z, "z", (B, N, N, self.D))
+        if mask is not None:
+            self._check_tensor(mask, "mask", (B, N, N))
+        if out is None:
+            out = torch.empty_like(z)
+        ws = self.workspace(B, N, z.device)
+        trimul_fwd(self.h, z, mask, direction, out, ws, stream)
+        return out
+
+    __call__ = forward
+
+    def project(self, z, mask=None, direction="outgoing"):
+        import torch
+        B, N = int(z.shape[0]), int(z.shape[1])
+        a = torch.empty((B, self.C, N, N), dtype=self.tdtype, device=z.device)
+        b = torch.empty_like(a)
+        trimul_internal_project(self.h, z, mask, direction, a, b)
+        return a, b
+
+    def contract(self, a_cm, b_cm):
+        import torch
+        o = torch.empty_like(a_cm)
+        trimul_internal_contract(self.h, a_cm, b_cm, o)
+        return o
+
+    def output(self, z, o):
+        import torch
+        out = torch.empty_like(z)
+        trimul_internal_output(self.h, z, o, out)
+        return out
+
+    def close(self):
+        if getattr(self, "h", None):
+            trimul_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,39 @@
+// trimul_launch.hpp -- host-side launchers of the three TriMul kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace trimul {
+
+enum class DType { BF16 = 0, FP32 = 1 };
+
+// Device-resident packed parameters (owned by the handle).
+struct Params {
+    int D, C;
+    DType dtype;
+    float eps;
+    // [4C][D]: for a then b, per 16-channel group g: 16 rows of p_in then the
+    // same 16 channels' rows of g_in.  The projection kernel's 64-row weight
+    // stage therefore holds (p, g) for 32 channels of one of a or b.
+    const void* w_proj;
+    const void* w_gout;    // [D][D]  g_out, rows = output channel
+    const void* w_pout;    // [D][C]  p_out, rows = output channel
+    const float* ln_in_w;  // [D]
+    const float* ln_in_b;  // [D]
+    const float* ln_out_w; // [C]
+    const float* ln_out_b; // [C]
+};
+
+hipError_t launch_project(const Params& p, const void* z, const void* mask, int B, int N,
+                          int incoming, void* a_cm, void* b_cm, hipStream_t s);
+hipError_t launch_contract(const Params& p, const void* a_cm, const void* b_cm, int B, int N,
+                           void* o, hipStream_t s);
+hipError_t launch_output(const Params& p, const void* z, const void* o, int B, int N, void* out,
+                         hipStream_t s);
+
+// Host mirrors of the kernels' static launch geometry (used for validation).
+bool project_supported(int D, int C, DType t);
+bool output_supported(int D, int C, DType t);
+
+}  // namespace trimul

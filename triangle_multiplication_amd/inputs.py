@@ -152,13 +152,21 @@ def pair_mask(token_mask, B, dtype="bf16", device="cpu"):
 
 
 def sample_grid(N, n=64, seed=SAMPLE_SEED, extra=()):
-    """Sorted distinct indices: 0, N-1, ``extra`` and seeded fill-ins, ``min(n, N)`` in all."""
+    """Two sorted index sets (rows I, columns J) of ``min(n, N)`` distinct tokens each.
+
+    Both contain 0, N-1 and ``extra``; the rest are drawn from one generator
+    seeded with ``seed`` (I first, then J).
+    """
     n = min(n, N)
     must = sorted({0, N - 1, *[int(e) for e in extra if 0 <= int(e) < N]})
     rng = np.random.default_rng(seed)
     pool = np.setdiff1d(np.arange(N), np.array(must))
-    fill = rng.choice(pool, size=max(0, n - len(must)), replace=False) if len(pool) else []
-    return np.sort(np.concatenate([np.array(must, np.int64), np.asarray(fill, np.int64)]))
+    out = []
+    for _ in range(2):
+        k = max(0, n - len(must))
+        fill = rng.choice(pool, size=k, replace=False) if k else np.zeros(0, np.int64)
+        out.append(np.sort(np.concatenate([np.array(must, np.int64), fill.astype(np.int64)])))
+    return out[0], out[1]
 
 
 @dataclass
