@@ -10,6 +10,10 @@ import ctypes
 import os
 
 import numpy as np
+# torch must be loaded first: its HIP runtime (libamdhip64, SONAME .so.7) is the
+# one libtrimul binds to.  Loading libtrimul first would pull in a second copy
+# of the runtime from /opt/rocm, which then finds no device.
+import torch  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtrimul.so")
@@ -138,13 +142,13 @@ def trimul_fwd(h, z, mask, direction, out, workspace, stream=None):
     """Enqueue the forward pass on ``stream`` (default: torch's current stream)."""
     B, N = int(z.shape[0]), int(z.shape[1])
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(_lib.trimul_fwd(h, _ptr(z), _ptr(mask), B, N, DIRECTIONS[direction], _ptr(out),
+    _check(_lib.trimul_fwd(h, _ptr(z), _ptr(mask), B, N, DIRECTIONS.get(direction, direction), _ptr(out),
                            _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def trimul_internal_project(h, z, mask, direction, a_cm, b_cm, stream=None):
     B, N = int(z.shape[0]), int(z.shape[1])
-    _check(_lib.trimul_internal_project(h, _ptr(z), _ptr(mask), B, N, DIRECTIONS[direction],
+    _check(_lib.trimul_internal_project(h, _ptr(z), _ptr(mask), B, N, DIRECTIONS.get(direction, direction),
                                         _ptr(a_cm), _ptr(b_cm), _stream(stream)))
 
 
