@@ -103,7 +103,8 @@ trimul_status trimul_workspace_query(int D, int C, trimul_dtype dtype, int B, in
  *   out        [B][N][N][D] device, 16-byte aligned; must not overlap z, the
  *              mask or the workspace.
  *   workspace  device, >= trimul_workspace_size bytes, 256-byte aligned.
- * Requires B >= 1, N >= 8, N % 8 == 0, B * C <= 65535, N <= 32768.
+ * Requires B >= 1, N >= 8, N % 8 == 0, N <= 32768, B * C <= 65535 and
+ * B * N * N < 2^31.
  */
 trimul_status trimul_fwd(trimul_handle *h, const void *z, const void *pair_mask, int B, int N,
                          trimul_direction dir, void *out, void *workspace,

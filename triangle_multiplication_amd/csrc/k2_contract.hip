@@ -33,11 +33,27 @@ __global__ __launch_bounds__(256) void k2_contract(const T* __restrict__ A, cons
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const size_t slab = (size_t)N * N;
-    const size_t bc = blockIdx.y;
+    // Tile order.  Workgroups are handed to the 8 XCDs round-robin by id, so id g
+    // runs on XCD g % 8.  Give each XCD a contiguous range of logical tiles
+    // (channel-major), and inside a channel walk groups of GM tile rows column by
+    // column: the ~32 tiles an XCD runs at once then share GM row panels of a and
+    // a few column panels of b in that XCD's L2.
+    const int tiles_i = (N + BM - 1) / BM;
+    const int per_bc = tiles_i * tiles_j;
+    const unsigned total = gridDim.x;                 // B*C*per_bc, a multiple of 8
+    const unsigned g = blockIdx.x;
+    const unsigned logical = (g & 7u) * (total >> 3) + (g >> 3);
+    const size_t bc = logical / per_bc;
+    const int t = (int)(logical % per_bc);
+    constexpr int GM = 4;
+    const int group = t / (GM * tiles_j);
+    const int first_i = group * GM;
+    const int gm = min(GM, tiles_i - first_i);
+    const int ti = first_i + (t % (GM * tiles_j)) % gm;
+    const int tj = (t % (GM * tiles_j)) / gm;
     const T* Ab = A + bc * slab;
     const T* Bb = Bm + bc * slab;
     T* Ob = O + bc * slab;
-    const int ti = blockIdx.x / tiles_j, tj = blockIdx.x % tiles_j;
     const int i0 = ti * BM, j0 = tj * BN;
 
     u32x4 ra[A_LD], rb[B_LD];
@@ -119,12 +135,180 @@ __global__ __launch_bounds__(256) void k2_contract(const T* __restrict__ A, cons
     }
 }
 
+// ---------------------------------------------------------------------------
+// Large-N bf16 path: 256 x 256 tiles fed by LDS DMA.
+//
+// K advances 32 per step.  The operand rows of a step (64 bytes each, 256 rows
+// of a and 256 of b = 32 KB) live in a ring of LDS slots filled by
+// buffer_load ... lds (global -> LDS without registers); offsets past the end of
+// the slab read as zero, which covers ragged rows and the K tail, and lets the
+// ring run past the last step without tail code.
+//
+// LDS layout of one operand in one slot (256 rows x 4 chunks of 16 bytes):
+// rows are paired into 128-byte lines, line L = row / 2 holds the 16-byte slot
+// ((row % 2) * 4 + chunk) ^ (L % 8).  For the MFMA fragment read (lane l: row
+// l % 16 of a 16-row block, chunk l / 16) this is free of LDS bank conflicts on
+// gfx950 (measured: 4 cycles per ds_read_b128, the rate of a contiguous read),
+// and each 1 KB DMA write is contiguous.
+// The compiler does not order LDS DMA against ds_read, so every hand-off is an
+// explicit s_waitcnt + s_barrier.
+// ---------------------------------------------------------------------------
+namespace k2big {
+constexpr int BM = 256, BN = 256, BK = 32;
+constexpr int ROWB = 64;                       // bytes of one operand row per step
+constexpr int OPB = BM * ROWB;                 // bytes of one operand per slot (16 KB)
+constexpr int STB = 2 * OPB;                   // bytes per slot (a and b)
+
+__device__ inline int slot_off(int row, int chunk)
+{
+    const int L = row >> 1;
+    return L * 128 + (((((row & 1) << 2) | chunk) ^ (L & 7)) << 4);
+}
+}  // namespace k2big
+
+#define TRIMUL_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+// 8 waves in a 2 x 4 grid, each owning a 128 x 64 block of the tile (8 x 4
+// MFMA tiles, 128 accumulators per lane); the two waves that share a SIMD
+// (wave w and w + 4) run half a step apart ("ping-pong").  Each wave
+// alternates a memory phase M_k (read step k's fragments from LDS, issue its
+// share of step k+3's DMA) and a compute phase C_k (32 MFMAs); group 0 (waves
+// 0-3) is one phase ahead of group 1 (waves 4-7), so in every phase one wave of
+// each SIMD multiplies while the other loads, and phases are separated by one
+// workgroup barrier.
+//
+// Phase p: group 0 runs M_{p/2} (p even) or C_{(p-1)/2} (p odd); group 1 runs
+// the same one phase later.  Invariants (NS = 4 slots, DMA three steps ahead):
+//  - step k's slot is read in phases 2k (group 0) and 2k+1 (group 1); every
+//    wave's DMA share of step k was issued at least four phases earlier, and
+//    before each barrier a wave waits until at most two of its steps are in
+//    flight, so step k has landed for everyone when phase 2k starts;
+//  - step k+3's DMA overwrites step k-1's slot, first in phase 2k, after the
+//    barrier that ends phase 2k-1 where the last reader (group 1) finished; a
+//    memory phase ends with lgkmcnt(0) so its reads are complete at that barrier.
+// Group 1 takes one extra barrier at the start and group 0 one at the end, so
+// every wave executes the same number of barriers.
+template <int NSP>
+__global__ __launch_bounds__(512) void k2_contract_pp(const bf16* __restrict__ A,
+                                                      const bf16* __restrict__ Bm,
+                                                      bf16* __restrict__ O, int N)
+{
+    using namespace k2big;
+    constexpr int NW = 8;
+    constexpr int DPO = OPB / 1024 / NW;            // DMA instructions per wave per operand (2)
+    constexpr int DPS = 2 * DPO;                    // per wave per step
+    constexpr int DIST = NSP - 1;                   // DMA runs this many steps ahead
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[NSP * STB];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 2, wn = wave & 3;        // group = wm
+    const size_t slab = (size_t)N * N;
+
+    const int tiles = (N + BM - 1) / BM;
+    const int per_bc = tiles * tiles;
+    const unsigned total = gridDim.x;
+    const unsigned g = blockIdx.x;
+    const unsigned logical = (g & 7u) * (total >> 3) + (g >> 3);
+    const size_t bc = logical / per_bc;
+    const int t = (int)(logical % per_bc);
+    constexpr int GM = 4;
+    const int first_i = (t / (GM * tiles)) * GM;
+    const int gm = min(GM, tiles - first_i);
+    const int ti = first_i + (t % (GM * tiles)) % gm;
+    const int tj = (t % (GM * tiles)) / gm;
+    const int i0 = ti * BM, j0 = tj * BN;
+
+    const unsigned nrec = (unsigned)(slab * sizeof(bf16));
+    __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)(A + bc * slab), 0, nrec, 0x00020000);
+    __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void*)(Bm + bc * slab), 0, nrec, 0x00020000);
+
+    const int dpos = (lane & 7) ^ (lane >> 3);
+    const int dr = 2 * (lane >> 3) + (dpos >> 2), dc = dpos & 3;
+    const unsigned qstride = (unsigned)N * 32u;
+    const unsigned offa0 = (unsigned)(i0 + wave * 16 * DPO + dr) * (unsigned)N * 2u + dc * 16u;
+    const unsigned offb0 = (unsigned)(j0 + wave * 16 * DPO + dr) * (unsigned)N * 2u + dc * 16u;
+    const int nk = (N + BK - 1) / BK;
+
+    auto issue = [&](int step) {
+        unsigned char* st = smem + (step % NSP) * STB + wave * DPO * 1024;
+        const int k0 = step * BK;
+        const unsigned kb = (unsigned)k0 * 2u;
+        const unsigned kpen = (k0 + dc * 8 < N) ? 0u : 0x80000000u;
+#pragma unroll
+        for (int q = 0; q < DPO; ++q) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, TRIMUL_LDS_PTR(st + q * 1024), 16,
+                                                     (offa0 + q * qstride + kb) | kpen, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, TRIMUL_LDS_PTR(st + OPB + q * 1024), 16,
+                                                     (offb0 + q * qstride + kb) | kpen, 0, 0, 0);
+        }
+    };
+
+    const int rchunk = lane >> 4;
+    const int fa_base = slot_off(wm * 128 + (lane & 15), rchunk);
+    const int fb_base = OPB + slot_off(wn * 64 + (lane & 15), rchunk);
+
+    f32x4 acc[8][4];
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int n = 0; n < 4; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    u32x4 fa[8], fb[4];
+    // Nothing may be scheduled across a phase boundary (MFMAs included).
+    auto barrier = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+#pragma unroll
+    for (int s0 = 0; s0 < DIST; ++s0) issue(s0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm((DIST - 1) * DPS));   // own share of step 0 landed
+    barrier();                                          // ... everyone's
+    if (wm == 1) barrier();                             // group 1 starts one phase late
+
+    for (int step = 0; step < nk; ++step) {
+        // M_step
+        const unsigned char* st = smem + (step % NSP) * STB;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) fa[m] = *reinterpret_cast<const u32x4*>(st + fa_base + m * 1024);
+#pragma unroll
+        for (int n = 0; n < 4; ++n) fb[n] = *reinterpret_cast<const u32x4*>(st + fb_base + n * 1024);
+        issue(step + DIST);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lds0((DIST - 1) * DPS));
+        barrier();
+        // C_step.  Operands swapped (b rows as the MFMA's A): each lane's four
+        // results are four consecutive j of one i.
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+            for (int n = 0; n < 4; ++n) acc[m][n] = Elem<bf16>::mma(fb[n], fa[m], acc[m][n]);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm((DIST - 1) * DPS));
+        barrier();
+    }
+    if (wm == 0) barrier();                             // balance group 1's extra barrier
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));          // no DMA may outlive the workgroup
+
+    bf16* Ob = O + bc * slab;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const int i = i0 + wm * 128 + m * 16 + (lane & 15);
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+            const int j = j0 + wn * 64 + n * 16 + 4 * (lane >> 4);
+            if (i < N && j < N) Elem<bf16>::store4(Ob, (size_t)i * N + j, acc[m][n]);
+        }
+    }
+}
+
 template <typename T, int BM, int BN>
 static hipError_t launch_k2(const void* a, const void* b, int B, int C, int N, void* o,
                             hipStream_t s)
 {
     const int tiles_i = (N + BM - 1) / BM, tiles_j = (N + BN - 1) / BN;
-    dim3 grid((unsigned)(tiles_i * tiles_j), (unsigned)(B * C));
+    dim3 grid((unsigned)((size_t)tiles_i * tiles_j * B * C));
     hipLaunchKernelGGL((k2_contract<T, BM, BN>), grid, dim3(256), 0, s,
                        (const T*)a, (const T*)b, (T*)o, N, tiles_j);
     return hipGetLastError();
@@ -133,6 +317,15 @@ static hipError_t launch_k2(const void* a, const void* b, int B, int C, int N, v
 hipError_t launch_contract(const Params& p, const void* a_cm, const void* b_cm, int B, int N,
                            void* o, hipStream_t s)
 {
+    // 256 x 256 DMA-fed tiles once N fills them; smaller N wastes less with 128 x 128.
+    const bool big = N >= 1024 && (N % 256 == 0 || N >= 2048);
+    if (p.dtype == DType::BF16 && big) {
+        const int tiles = (N + k2big::BM - 1) / k2big::BM;
+        dim3 grid((unsigned)((size_t)tiles * tiles * B * p.C));
+        hipLaunchKernelGGL(k2_contract_pp<4>, grid, dim3(512), 0, s, (const bf16*)a_cm,
+                           (const bf16*)b_cm, (bf16*)o, N);
+        return hipGetLastError();
+    }
     if (p.dtype == DType::BF16) return launch_k2<bf16, 128, 128>(a_cm, b_cm, B, p.C, N, o, s);
     return launch_k2<float, 128, 128>(a_cm, b_cm, B, p.C, N, o, s);
 }

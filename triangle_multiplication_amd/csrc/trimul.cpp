@@ -86,6 +86,9 @@ trimul_status check_shape(const trimul_handle* h, int B, int N)
     if (N > 32768) return fail(TRIMUL_ERR_UNSUPPORTED, "N must be <= 32768; got %d", N);
     if ((long long)B * h->p.C > 65535)
         return fail(TRIMUL_ERR_UNSUPPORTED, "B*C must be <= 65535; got %lld", (long long)B * h->p.C);
+    // Every launch covers at most 2 threads per pair; keep that below 2^32.
+    if ((long long)B * N * N >= (1LL << 31))
+        return fail(TRIMUL_ERR_UNSUPPORTED, "B*N*N must be < 2^31; got %lld", (long long)B * N * N);
     return TRIMUL_OK;
 }
 

@@ -106,4 +106,10 @@ __device__ inline int swz(int row, int chunk) { return chunk ^ (row & 7); }
 // swizzled index inside the row (n is a multiple of 4 for all widths used).
 constexpr int swz_mask(int n) { return n % 8 == 0 ? 7 : n % 4 == 0 ? 3 : n % 2 == 0 ? 1 : 0; }
 
+// s_waitcnt immediate for "vmcnt <= n" leaving expcnt and lgkmcnt unconstrained
+// (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+constexpr int waitcnt_vm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4) | (15 << 8); }
+// ... and additionally "lgkmcnt == 0" (every LDS read of this wave has completed).
+constexpr int waitcnt_vm_lds0(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4); }
+
 }  // namespace trimul
