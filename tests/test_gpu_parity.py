@@ -125,7 +125,8 @@ def test_project_stage(tb, dtype, direction, B, N, D, C):
 # Output kernel alone against the oracle's output stage
 # ----------------------------------------------------------------------------
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
-@pytest.mark.parametrize("B,N,D,C", [(1, 24, 64, 64), (2, 40, 32, 96), (1, 16, 256, 256), (1, 8, 160, 224)])
+@pytest.mark.parametrize("B,N,D,C", [(1, 24, 64, 64), (2, 40, 32, 96), (1, 16, 256, 256), (1, 8, 160, 224),
+                                     (1, 72, 128, 128), (2, 16, 128, 128), (2, 24, 256, 256)])
 def test_output_stage(tb, dtype, B, N, D, C):
     say("output stage", dtype, B, N, D, C)
     w = inputs.make_weights(D, C, dtype, random_ln=True)

@@ -199,6 +199,272 @@ __global__ __launch_bounds__(256) void k3_output(
     }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 path for D = C in {128, 256}: persistent, LayerNorm folded into the
+// output GEMMs, weights resident in registers, activations in an LDS ring.
+//
+// Both LayerNorms are applied algebraically instead of element by element.
+// For a row v of length L with mean mu and rstd = 1 / sqrt(var + eps), and a
+// weight row W acting on gamma * (v - mu) * rstd + beta:
+//   W (gamma (v - mu) rstd + beta) = rstd (W' v - mu S + T sd),
+//   W' = gamma-scaled W (rounded to bf16), S = sum of W' row, T = W beta,
+//   sd = 1 / rstd.
+// The matrix cores multiply W' with the raw bf16 rows of z and o, and one
+// extra MFMA per output block adds -mu S + T sd from a K-group whose lane
+// group 0 holds mu and sd split into bf16 high and low parts (six products:
+// mu_h S_h, mu_h S_l, mu_l S_h, sd_h T_h, sd_h T_l, sd_l T_h; the host
+// supplies S and T split the same way) and whose other lanes hold zeros.  It
+// is the first MFMA of each accumulation chain.  (The 16x16x16 bf16 MFMA
+// would need fewer registers, but this compiler under-counts its latency on
+// gfx950 and lets a VALU read its result too early.)  Statistics take one pass with
+// v_dot2_f32_bf16 (sum and sum of squares, var = E[v^2] - mu^2 in fp32).
+// The epilogue is then out = (rstd_o acc_p) / (1 + 2^(-log2(e) rstd_x acc_g)).
+//
+// One 512-thread workgroup per CU walks 32-pair tiles; the two halves of each
+// 64-pair run go to the same CU back to back, so the second half of every
+// 128-byte line of o is an L2 hit.  Each of the 8 waves owns 16-row blocks
+// rb = wave + 8 r of the D output channels and holds those rows of W'_g and
+// W'_p in registers for the whole kernel.  A ring of four LDS slots, filled by
+// global->LDS DMA three tiles ahead, holds per tile
+//   z: 32 rows of 2D bytes, 16-byte chunk c of row p stored at c ^ (p % 16);
+//   o: C channel rows of 64 bytes (32 pairs), 32-byte half h of row c stored at
+//      h ^ ((c >> 3) & 1), so ds_read_b64_tr_b16 reads of a 32-lane half touch
+//      distinct banks.
+// Per tile t: waves 0..3 compute the statistics of tile t + 1 (one of the two
+// 16-pair blocks of z or of o each) into a double-buffered LDS record; then all
+// waves run the MFMAs and the epilogue of tile t; one barrier ends the tile.
+// ---------------------------------------------------------------------------
+namespace k3f {
+constexpr int TM = 32, NB = TM / 16, NW = 8, NS = 4;
+constexpr float LOG2E = 1.4426950408889634f;
+
+template <int D, int C>
+struct Cfg {
+    static constexpr int KGD = D / 32, KGC = C / 32;
+    static constexpr int RBT = D / 16, RBW = RBT / NW;      // 16-row output blocks (per wave)
+    static constexpr int ZB = TM * D * 2, OB = C * TM * 2;   // slot bytes of z and of o
+    static constexpr int SLOT = ZB + OB;
+    static constexpr int ZDMA = ZB / 1024, DMA_ALL = (ZB + OB) / 1024;
+    static constexpr int DPW = DMA_ALL / NW;                  // 1 KB DMA instructions per wave per tile
+    static constexpr int STORES = NB * RBW;                   // global stores per wave per tile
+    static constexpr int FRAG = 1024;                         // one extra K-group fragment
+    static constexpr int STAT = 4 * FRAG + 4 * 64;            // [kind][block] fragments + scales
+    static constexpr int LDS = NS * SLOT + 2 * STAT;
+    static_assert(D % 32 == 0 && C % 32 == 0 && D >= 128 && RBT % NW == 0, "widths");
+    static_assert(DMA_ALL % NW == 0 && ZB % 1024 == 0 && OB % 1024 == 0, "DMA split");
+    static_assert(LDS <= 160 * 1024, "LDS");
+};
+}  // namespace k3f
+
+#define TRIMUL_LDS3(p) ((__attribute__((address_space(3))) void*)(p))
+
+template <int D, int C>
+__global__ __launch_bounds__(512) void k3_output_fold(
+    const bf16* __restrict__ z, const bf16* __restrict__ o, const bf16* __restrict__ Wg,
+    const bf16* __restrict__ Wp, const bf16* __restrict__ Xg, const bf16* __restrict__ Xp,
+    float eps, bf16* __restrict__ out, int N, int n_super)
+{
+    using namespace k3f;
+    using Cf = Cfg<D, C>;
+    constexpr int KGD = Cf::KGD, KGC = Cf::KGC, RBW = Cf::RBW;
+    constexpr int ZB = Cf::ZB, SLOT = Cf::SLOT, FRAG = Cf::FRAG, STAT = Cf::STAT;
+    typedef short i16x4 __attribute__((ext_vector_type(4)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[Cf::LDS];
+    unsigned char* ring = smem;
+    unsigned char* stat = smem + NS * SLOT;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const size_t NN = (size_t)N * N;
+    const int G = gridDim.x, g = blockIdx.x;
+    // This workgroup's tiles: 64-pair runs g, g + G, ..., each as two 32-pair halves.
+    const int n_tiles = 2 * ((n_super - g + G - 1) / G);
+    auto tile_p0 = [&](int it) -> size_t {
+        return it < n_tiles ? ((size_t)(g + (it >> 1) * G) * 64 + (it & 1) * 32) : 0;
+    };
+
+    // Weight rows of this wave (MFMA A operand: lane = row l16 of the block,
+    // chunk g4 of each K-group); the extra K-group uses lanes g4 == 0.
+    u32x4 wg[RBW][KGD], wp[RBW][KGC];
+    u32x4 xg[RBW], xp[RBW];
+#pragma unroll
+    for (int r = 0; r < RBW; ++r) {
+        const int d = (wave + r * NW) * 16 + l16;
+#pragma unroll
+        for (int kg = 0; kg < KGD; ++kg) wg[r][kg] = ld16(Wg + (size_t)d * D + (kg * 4 + g4) * 8);
+#pragma unroll
+        for (int kg = 0; kg < KGC; ++kg) wp[r][kg] = ld16(Wp + (size_t)d * C + (kg * 4 + g4) * 8);
+        const u32x4 zero4 = {0u, 0u, 0u, 0u};
+        xg[r] = g4 == 0 ? ld16(Xg + d * 8) : zero4;
+        xp[r] = g4 == 0 ? ld16(Xp + d * 8) : zero4;
+    }
+
+    // DMA of tile it into ring slot it % NS.  Instruction q covers 1 KB of the
+    // slot; lane l fills its 16 bytes.  Phantom tiles (past the end) re-read
+    // tile 0 so that every wave issues the same count.
+    auto issue = [&](int it) {
+        const size_t p0 = tile_p0(it);
+        const size_t bidx = p0 / NN, pin = p0 % NN;
+        unsigned char* sl = ring + (it & (NS - 1)) * SLOT;
+        int ln = threadIdx.x & 63;      // opaque: keeps per-lane offsets out of loop-carried registers
+        asm volatile("" : "+v"(ln));
+#pragma unroll
+        for (int i = 0; i < Cf::DPW; ++i) {
+            const int q = wave + i * NW;
+            if (q < Cf::ZDMA) {
+                const int byte = q * 1024 + ln * 16;
+                const int row = byte / (D * 2), pch = (byte % (D * 2)) / 16;
+                const bf16* src = z + (p0 + row) * D + (pch ^ (row & 15)) * 8;
+                __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                                 TRIMUL_LDS3(sl + q * 1024), 16, 0, 0);
+            } else {
+                const int qo = q - Cf::ZDMA;
+                const int c = qo * 16 + (ln >> 2), pc = ln & 3;
+                const int half = (pc >> 1) ^ ((c >> 3) & 1);
+                const bf16* src = o + (bidx * C + c) * NN + pin + half * 16 + (pc & 1) * 8;
+                __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                                 TRIMUL_LDS3(sl + ZB + qo * 1024), 16, 0, 0);
+            }
+        }
+    };
+    auto barrier = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // Fragment addressing.  z, block bb, K-group kg: lane reads chunk
+    // (4 kg + g4) ^ l16 of row 16 bb + l16, i.e. zb[kg & 3] + 256 (kg >> 2) + 32 D bb.
+    int zb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) zb[j] = l16 * (2 * D) + ((g4 ^ (l16 & 3)) * 16) + ((j ^ (l16 >> 2)) << 6);
+    // o, block bb, K-group kg, half hh: channel row kg*32 + 8 g4 + 4 hh + l16/4,
+    // pairs 16 bb + 4 (l16 % 4) .. +3, i.e. ob_[bb] + 256 hh + 2048 kg.
+    int obb[NB];
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb)
+        obb[bb] = (g4 * 8 + (l16 >> 2)) * 64 + ((bb ^ (g4 & 1)) * 32) + (l16 & 3) * 8;
+    auto zfrag = [&](const unsigned char* sl, int bb, int kg) -> u32x4 {
+        return *reinterpret_cast<const u32x4*>(sl + zb[kg & 3] + 256 * (kg >> 2) + 32 * D * bb);
+    };
+    auto ofrag = [&](const unsigned char* sl, int bb, int kg) -> u32x4 {
+        const unsigned char* p = sl + ZB + obb[bb] + 2048 * kg;
+        const i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
+        const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p + 256));
+        const u32x2 h0 = __builtin_bit_cast(u32x2, r0), h1 = __builtin_bit_cast(u32x2, r1);
+        return u32x4{h0[0], h0[1], h1[0], h1[1]};
+    };
+
+    // Statistics of one 16-pair block of tile it (waves 0..3: kind = wave / 2
+    // selects z or o, bb = wave % 2), written to record it % 2.
+    auto stats = [&](int it) {
+        const unsigned char* sl = ring + (it & (NS - 1)) * SLOT;
+        unsigned char* st = stat + (it & 1) * STAT;
+        const int kind = wave >> 1, bb = wave & 1;
+        const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+        float s1 = 0.f, s2 = 0.f;
+        auto acc = [&](u32x4 v) {
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                // Copy the element out first: bit_cast of a vector-element
+                // lvalue reads element 0 with this compiler.
+                const uint32_t w = v[h];
+                const bf16x2 x = __builtin_bit_cast(bf16x2, w);
+                s1 = __builtin_amdgcn_fdot2_f32_bf16(x, one2, s1, false);
+                s2 = __builtin_amdgcn_fdot2_f32_bf16(x, x, s2, false);
+            }
+        };
+        if (kind == 0) {
+#pragma unroll
+            for (int kg = 0; kg < KGD; ++kg) acc(zfrag(sl, bb, kg));
+        } else {
+#pragma unroll
+            for (int kg = 0; kg < KGC; ++kg) acc(ofrag(sl, bb, kg));
+        }
+        s1 = sum_row_lanes(s1);
+        s2 = sum_row_lanes(s2);
+        const float invL = kind == 0 ? 1.0f / D : 1.0f / C;
+        const float mu = s1 * invL;
+        const float ve = fmaxf(s2 * invL - mu * mu, 0.f) + eps;
+        const float rstd = rsqrtf(ve);
+        const float sd = ve * rstd;
+        const __bf16 nmh = (__bf16)(-mu), nml = (__bf16)(-mu - (float)nmh);
+        const __bf16 sdh = (__bf16)sd, sdl = (__bf16)(sd - (float)sdh);
+        const __bf16 zr = (__bf16)0.0f;
+        bf16x8 f = {zr, zr, zr, zr, zr, zr, zr, zr};
+        if (g4 == 0) f = bf16x8{nmh, nmh, nml, sdh, sdh, sdl, zr, zr};
+        *reinterpret_cast<bf16x8*>(st + (kind * NB + bb) * FRAG + lane * 16) = f;
+        if (g4 == 0)
+            *reinterpret_cast<float*>(st + 4 * FRAG + (kind * NB + bb) * 64 + l16 * 4) =
+                kind == 0 ? -rstd * LOG2E : rstd;
+    };
+
+    // MFMAs and epilogue of tile it.
+    auto compute = [&](int it) {
+        const unsigned char* sl = ring + (it & (NS - 1)) * SLOT;
+        const unsigned char* st = stat + (it & 1) * STAT;
+        bf16* ob = out + tile_p0(it) * D;
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) {
+            f32x4 ag[RBW], ay[RBW];
+            const u32x4 xe = *reinterpret_cast<const u32x4*>(st + bb * FRAG + lane * 16);
+            const u32x4 ye = *reinterpret_cast<const u32x4*>(st + (NB + bb) * FRAG + lane * 16);
+#pragma unroll
+            for (int r = 0; r < RBW; ++r) {
+                const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+                ag[r] = Elem<bf16>::mma(xg[r], xe, z4);
+                ay[r] = Elem<bf16>::mma(xp[r], ye, z4);
+            }
+#pragma unroll
+            for (int kg = 0; kg < KGD; ++kg) {
+                const u32x4 xf = zfrag(sl, bb, kg);
+#pragma unroll
+                for (int r = 0; r < RBW; ++r) ag[r] = Elem<bf16>::mma(wg[r][kg], xf, ag[r]);
+            }
+#pragma unroll
+            for (int kg = 0; kg < KGC; ++kg) {
+                const u32x4 yf = ofrag(sl, bb, kg);
+#pragma unroll
+                for (int r = 0; r < RBW; ++r) ay[r] = Elem<bf16>::mma(wp[r][kg], yf, ay[r]);
+            }
+            const float cx = *reinterpret_cast<const float*>(st + 4 * FRAG + bb * 64 + l16 * 4);
+            const float ro = *reinterpret_cast<const float*>(st + 4 * FRAG + (NB + bb) * 64 + l16 * 4);
+            // Lane holds output channels rb*16 + 4*g4 + 0..3 of pair 16*bb + l16.
+#pragma unroll
+            for (int r = 0; r < RBW; ++r) {
+                f32x4 res;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    res[e] = ro * ay[r][e] * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(cx * ag[r][e]));
+                Elem<bf16>::store4(ob, (size_t)(bb * 16 + l16) * D + (wave + r * NW) * 16 + 4 * g4, res);
+            }
+        }
+    };
+
+    issue(0);
+    issue(1);
+    issue(2);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lds0(2 * Cf::DPW));   // tile 0 landed (own share)
+    barrier();                                                   // ... everyone's
+    if (wave < 4) stats(0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lds0(Cf::DPW));       // tile 1 landed
+    barrier();
+    for (int it = 0; it < n_tiles; ++it) {
+        issue(it + 3);                 // into the slot tile it - 1 used
+        if (wave < 4) stats(it + 1);
+        compute(it);
+        // Tile it + 2 must have landed: after its DMA this wave issued at most
+        // the stores of tiles it - 1 and it and the DMA of tile it + 3; waiting
+        // also for the stores of tile it - 1 costs nothing.
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lds0(Cf::DPW + Cf::STORES));
+        barrier();
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // no DMA may outlive the workgroup
+}
+
 template <typename T, int D, int C>
 static hipError_t launch_k3_t(const Params& p, const void* z, const void* o, int B, int N,
                               void* out, hipStream_t s)
@@ -226,6 +492,22 @@ static hipError_t launch_k3_t(const Params& p, const void* z, const void* o, int
     default: return hipErrorInvalidValue;                                                 \
     }
 
+template <int D, int C>
+static hipError_t launch_k3_fold(const Params& p, const void* z, const void* o, int B, int N,
+                                 void* out, hipStream_t s)
+{
+    const long long n_super = (long long)B * N * N / 64;   // N % 8 == 0, so N*N % 64 == 0
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess)
+        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const long long grid = n_super < cus ? n_super : cus;
+    hipLaunchKernelGGL((k3_output_fold<D, C>), dim3((unsigned)grid), dim3(512), 0, s, (const bf16*)z,
+                       (const bf16*)o, (const bf16*)p.w_gout_f, (const bf16*)p.w_pout_f,
+                       (const bf16*)p.x_gout, (const bf16*)p.x_pout, p.eps, (bf16*)out, N,
+                       (int)n_super);
+    return hipGetLastError();
+}
+
 template <typename T>
 static hipError_t launch_k3_d(const Params& p, const void* z, const void* o, int B, int N,
                               void* out, hipStream_t s)
@@ -251,6 +533,10 @@ bool output_supported(int D, int C, DType)
 hipError_t launch_output(const Params& p, const void* z, const void* o, int B, int N, void* out,
                          hipStream_t s)
 {
+    if (p.dtype == DType::BF16 && p.D == 256 && p.C == 256)
+        return launch_k3_fold<256, 256>(p, z, o, B, N, out, s);
+    if (p.dtype == DType::BF16 && p.D == 128 && p.C == 128)
+        return launch_k3_fold<128, 128>(p, z, o, B, N, out, s);
     if (p.dtype == DType::BF16) return launch_k3_d<bf16>(p, z, o, B, N, out, s);
     return launch_k3_d<float>(p, z, o, B, N, out, s);
 }

@@ -68,6 +68,37 @@ uint16_t f32_to_bf16(float f)
     return (uint16_t)(u >> 16);
 }
 
+float bf16_to_f32(uint16_t h)
+{
+    const uint32_t u = (uint32_t)h << 16;
+    float f;
+    std::memcpy(&f, &u, 4);
+    return f;
+}
+
+// Folded output GEMM for the bf16 kernels that apply LayerNorm algebraically:
+// rows d of W (rows x K, fp32) become bf16(W[d][k] * gamma[k]), and each row
+// gets the correction terms S_d = sum_k of the folded bf16 row and
+// T_d = sum_k W[d][k] * beta[k], each split as high = bf16(v), low = bf16(v - high).
+void fold_rows(const float* W, const float* gamma, const float* beta, int rows, int K,
+               uint16_t* wf, uint16_t* x)
+{
+    for (int d = 0; d < rows; ++d) {
+        double S = 0.0, T = 0.0;
+        for (int k = 0; k < K; ++k) {
+            const uint16_t h = f32_to_bf16((float)((double)W[(size_t)d * K + k] * gamma[k]));
+            wf[(size_t)d * K + k] = h;
+            S += bf16_to_f32(h);
+            T += (double)W[(size_t)d * K + k] * beta[k];
+        }
+        const uint16_t sh = f32_to_bf16((float)S), th = f32_to_bf16((float)T);
+        const uint16_t sl = f32_to_bf16((float)(S - bf16_to_f32(sh)));
+        const uint16_t tl = f32_to_bf16((float)(T - bf16_to_f32(th)));
+        const uint16_t row[8] = {sh, sl, sh, th, tl, th, 0, 0};
+        std::memcpy(x + (size_t)d * 8, row, sizeof row);
+    }
+}
+
 void put(std::vector<uint8_t>& dst, size_t off_elems, float v, trimul_dtype t)
 {
     if (t == TRIMUL_BF16) {
@@ -192,8 +223,21 @@ trimul_status trimul_create(int D, int C, trimul_dtype dtype, const trimul_weigh
     const size_t off_go = align256(n_proj * es);
     const size_t off_po = off_go + align256(n_go * es);
     const size_t off_ln = off_po + align256(n_po * es);
-    const size_t total = off_ln + align256((size_t)(2 * D + 2 * C) * 4);
+    const size_t off_gof = off_ln + align256((size_t)(2 * D + 2 * C) * 4);
+    const bool folded = dtype == TRIMUL_BF16;
+    const size_t off_pof = off_gof + (folded ? align256(n_go * 2) : 0);
+    const size_t off_xg = off_pof + (folded ? align256(n_po * 2) : 0);
+    const size_t off_xp = off_xg + (folded ? align256((size_t)D * 16) : 0);
+    const size_t total = off_xp + (folded ? align256((size_t)D * 16) : 0);
     std::vector<uint8_t> host(total, 0);
+    if (folded) {
+        fold_rows(w->g_out, w->norm_in_weight, w->norm_in_bias, D, D,
+                  reinterpret_cast<uint16_t*>(host.data() + off_gof),
+                  reinterpret_cast<uint16_t*>(host.data() + off_xg));
+        fold_rows(w->p_out, w->norm_out_weight, w->norm_out_bias, D, C,
+                  reinterpret_cast<uint16_t*>(host.data() + off_pof),
+                  reinterpret_cast<uint16_t*>(host.data() + off_xp));
+    }
     {
         std::vector<uint8_t> proj(n_proj * es), go(n_go * es), po(n_po * es);
         size_t row = 0;
@@ -246,6 +290,10 @@ trimul_status trimul_create(int D, int C, trimul_dtype dtype, const trimul_weigh
     h->p.ln_in_b = ln + D;
     h->p.ln_out_w = ln + 2 * D;
     h->p.ln_out_b = ln + 2 * D + C;
+    h->p.w_gout_f = folded ? base + off_gof : nullptr;
+    h->p.w_pout_f = folded ? base + off_pof : nullptr;
+    h->p.x_gout = folded ? base + off_xg : nullptr;
+    h->p.x_pout = folded ? base + off_xp : nullptr;
     *out = h;
     return ok();
 }

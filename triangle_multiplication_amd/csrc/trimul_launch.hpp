@@ -23,6 +23,15 @@ struct Params {
     const float* ln_in_b;  // [D]
     const float* ln_out_w; // [C]
     const float* ln_out_b; // [C]
+    // bf16 handles only (null otherwise): the output GEMMs with the LayerNorm
+    // scales folded in, for kernels that apply LayerNorm algebraically.
+    const void* w_gout_f;  // [D][D]  g_out[d][k] * ln_in_w[k]
+    const void* w_pout_f;  // [D][C]  p_out[d][c] * ln_out_w[c]
+    // [D][8] per output row: S_h, S_l, S_h, T_h, T_l, T_h, 0, 0, where S is the
+    // sum of the folded bf16 row, T the dot product of the unfolded row with the
+    // LayerNorm bias, each split into a bf16 high part and a bf16 remainder.
+    const void* x_gout;
+    const void* x_pout;
 };
 
 hipError_t launch_project(const Params& p, const void* z, const void* mask, int B, int N,
