@@ -228,7 +228,10 @@ trimul_status trimul_create(int D, int C, trimul_dtype dtype, const trimul_weigh
     const size_t off_pof = off_gof + (folded ? align256(n_go * 2) : 0);
     const size_t off_xg = off_pof + (folded ? align256(n_po * 2) : 0);
     const size_t off_xp = off_xg + (folded ? align256((size_t)D * 16) : 0);
-    const size_t total = off_xp + (folded ? align256((size_t)D * 16) : 0);
+    const size_t off_wpf = off_xp + (folded ? align256((size_t)D * 16) : 0);
+    const size_t off_xpj = off_wpf + (folded ? align256(n_proj * 2) : 0);
+    const size_t off_sink = off_xpj + (folded ? align256((size_t)4 * C * 16) : 0);
+    const size_t total = off_sink + 4096;
     std::vector<uint8_t> host(total, 0);
     if (folded) {
         fold_rows(w->g_out, w->norm_in_weight, w->norm_in_bias, D, D,
@@ -239,17 +242,24 @@ trimul_status trimul_create(int D, int C, trimul_dtype dtype, const trimul_weigh
                   reinterpret_cast<uint16_t*>(host.data() + off_xp));
     }
     {
-        std::vector<uint8_t> proj(n_proj * es), go(n_go * es), po(n_po * es);
+        std::vector<uint8_t> go(n_go * es), po(n_po * es);
+        // Projection rows in the kernels' order: for a then b, per 16-channel
+        // group, 16 rows of p_in then the same channels' 16 rows of g_in.
+        std::vector<float> projf(n_proj);
         size_t row = 0;
         for (int part = 0; part < 2; ++part)          // a, then b
             for (int g = 0; g < C / 16; ++g) {        // 16-channel groups
                 for (int r = 0; r < 16; ++r, ++row)   // p rows
-                    for (int d = 0; d < D; ++d)
-                        put(proj, row * D + d, w->p_in[((size_t)part * C + g * 16 + r) * D + d], dtype);
+                    std::memcpy(&projf[row * D], w->p_in + ((size_t)part * C + g * 16 + r) * D, D * 4);
                 for (int r = 0; r < 16; ++r, ++row)   // g rows of the same channels
-                    for (int d = 0; d < D; ++d)
-                        put(proj, row * D + d, w->g_in[((size_t)part * C + g * 16 + r) * D + d], dtype);
+                    std::memcpy(&projf[row * D], w->g_in + ((size_t)part * C + g * 16 + r) * D, D * 4);
             }
+        std::vector<uint8_t> proj(n_proj * es);
+        for (size_t i = 0; i < n_proj; ++i) put(proj, i, projf[i], dtype);
+        if (folded)
+            fold_rows(projf.data(), w->norm_in_weight, w->norm_in_bias, 4 * C, D,
+                      reinterpret_cast<uint16_t*>(host.data() + off_wpf),
+                      reinterpret_cast<uint16_t*>(host.data() + off_xpj));
         for (size_t i = 0; i < n_go; ++i) put(go, i, w->g_out[i], dtype);
         for (size_t i = 0; i < n_po; ++i) put(po, i, w->p_out[i], dtype);
         std::memcpy(host.data() + off_proj, proj.data(), proj.size());
@@ -294,6 +304,9 @@ trimul_status trimul_create(int D, int C, trimul_dtype dtype, const trimul_weigh
     h->p.w_pout_f = folded ? base + off_pof : nullptr;
     h->p.x_gout = folded ? base + off_xg : nullptr;
     h->p.x_pout = folded ? base + off_xp : nullptr;
+    h->p.w_proj_f = folded ? base + off_wpf : nullptr;
+    h->p.x_proj = folded ? base + off_xpj : nullptr;
+    h->p.sink = base + off_sink;
     *out = h;
     return ok();
 }

@@ -32,6 +32,13 @@ struct Params {
     // LayerNorm bias, each split into a bf16 high part and a bf16 remainder.
     const void* x_gout;
     const void* x_pout;
+    // The projection with ln_in_w folded in, rows in w_proj's order, and its
+    // [4C][8] correction rows (same form as x_gout).
+    const void* w_proj_f;
+    const void* x_proj;
+    // 4 KB of device memory that kernels with a fixed number of stores per
+    // step write their out-of-range lanes to; never read.
+    void* sink;
 };
 
 hipError_t launch_project(const Params& p, const void* z, const void* mask, int B, int N,
