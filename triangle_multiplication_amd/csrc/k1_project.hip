@@ -222,7 +222,9 @@ struct Cfg {
     static constexpr int DPW = STAGE / 1024 / NWV;             // DMA instructions per wave per stage
     static constexpr int EXT = 4 * CMAX * 16;                  // correction rows
     static constexpr int SC = NWV * RB * 2 * 16 * 4;           // per-pair scales
-    static constexpr int LDS = NSW * STAGE + EXT + SC;
+    static constexpr int XF = (NWV + 1) * RB * 16 * 16;        // correction fragments + zeros
+    static constexpr int OT = NWV * 16 * ROWS * 2;             // per-wave output tiles
+    static constexpr int LDS = NSW * STAGE + EXT + SC + XF + OT;
     static_assert(D == 128 || D == 256, "widths");
     static_assert(STAGE % (1024 * NWV) == 0, "DMA split");
 };
@@ -244,6 +246,16 @@ __global__ __launch_bounds__(256, 2) void k1_project_fold(
     unsigned char* ring = smem;
     u32x4* ext = reinterpret_cast<u32x4*>(smem + NSW * STAGE);
     float* sc = reinterpret_cast<float*>(smem + NSW * STAGE + Cf::EXT);
+    // Correction fragments: lane group 0 of block rb of wave w at
+    // xfa + (w * RB + rb) * 256 + l16 * 16; the last RB * 256 bytes are zeros,
+    // read by lane groups 1..3.
+    unsigned char* xfa = smem + NSW * STAGE + Cf::EXT + Cf::SC;
+    // This wave's output tile of one stage: 16 channel rows of 64 pairs (128
+    // bytes).  The 8-byte slot c of row r sits at c ^ (2 (r / 2)), so the
+    // epilogue's 8-byte writes (lanes = 16 rows x 2 slots per 32 lanes) and the
+    // 16-byte read-back (lanes = 2 rows x 8 chunks per 16 lanes) hit distinct
+    // banks.
+    unsigned char* otile = smem + NSW * STAGE + Cf::EXT + Cf::SC + Cf::XF + (threadIdx.x >> 6) * 16 * ROWS * 2;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, g4 = lane >> 4;
@@ -267,20 +279,28 @@ __global__ __launch_bounds__(256, 2) void k1_project_fold(
         mvalid = min(ROWS, N - r0);
     }
 
+    // Per-lane source offsets (elements) of this wave's DMA instructions within
+    // a stage: instruction qi = wave + 4 i fills bytes [qi KB, qi KB + 1 KB) of
+    // the slot, i.e. row r = 1024 qi / 2D + l / (2D / 16), physical chunk
+    // l % (2D / 16), holding logical chunk (physical ^ (r % 16)).  Row r grows
+    // by 2048 i / D, a multiple of 8, so offsets of instruction i are those of
+    // instruction i % 2 plus 16 (i / 2) rows.
+    uint32_t doff[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int qi = wave + i * NWV;
+        const int byte = qi * 1024 + lane * 16;
+        const int row = byte / (2 * D), pch = (byte % (2 * D)) / 16;
+        doff[i] = (uint32_t)(row * D + (pch ^ (row & 15)) * 8);
+    }
     auto issue = [&](int q) {
         const bf16* w0 = Wf + (size_t)q * 32 * D;
         unsigned char* sl = ring + (q % NSW) * STAGE;
-        int ln = threadIdx.x & 63;   // opaque: keeps per-lane offsets out of loop-carried registers
-        asm volatile("" : "+v"(ln));
 #pragma unroll
-        for (int i = 0; i < DPW; ++i) {
-            const int qi = wave + i * NWV;
-            const int byte = qi * 1024 + ln * 16;
-            const int row = byte / (2 * D), pch = (byte % (2 * D)) / 16;
-            const bf16* src = w0 + (size_t)row * D + (pch ^ (row & 15)) * 8;
-            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                             TRIMUL_K1_LDS3(sl + qi * 1024), 16, 0, 0);
-        }
+        for (int i = 0; i < DPW; ++i)
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void*)(w0 + (i >> 1) * 16 * D + doff[i & 1]),
+                TRIMUL_K1_LDS3(sl + (wave + i * NWV) * 1024), 16, 0, 0);
     };
     auto barrier = [&]() {
         __builtin_amdgcn_sched_barrier(0);
@@ -291,12 +311,17 @@ __global__ __launch_bounds__(256, 2) void k1_project_fold(
     };
 
     issue(0);
-    issue(1);   // NQ = C / 8 >= 4
+    issue(1);
+    issue(2);   // NQ = C / 8 >= 4
     for (int i = tid; i < 4 * C; i += 256) ext[i] = ld16(Xf + (size_t)i * 8);
+    if (wave == 0)
+#pragma unroll
+        for (int i = 0; i < RB * 16 * 16 / (64 * 16); ++i)
+            *reinterpret_cast<u32x4*>(xfa + NWV * RB * 256 + (i * 64 + lane) * 16) = u32x4{0u, 0u, 0u, 0u};
 
     // Raw z rows as the MFMA A operand: block rb, K-group kg -> chunk kg*4 + g4
     // of pair rb*16 + l16.  K-group KG is the correction fragment.
-    u32x4 zf[RB][KG + 1];
+    u32x4 zf[RB][KG];
     const u32x4 zero = {0u, 0u, 0u, 0u};
     const bf16* zb = z + (size_t)bidx * NN * D;
 #pragma unroll
@@ -335,17 +360,16 @@ __global__ __launch_bounds__(256, 2) void k1_project_fold(
         const __bf16 nmh = (__bf16)(-mu), nml = (__bf16)(-mu - (float)nmh);
         const __bf16 sdh = (__bf16)sd, sdl = (__bf16)(sd - (float)sdh);
         const __bf16 zr = (__bf16)0.0f;
-        bf16x8 f = {zr, zr, zr, zr, zr, zr, zr, zr};
-        if (g4 == 0) f = bf16x8{nmh, nmh, nml, sdh, sdh, sdl, zr, zr};
-        zf[rb][KG] = __builtin_bit_cast(u32x4, f);
         if (g4 == 0) {
+            *reinterpret_cast<bf16x8*>(xfa + (wave * RB + rb) * 256 + l16 * 16) =
+                bf16x8{nmh, nmh, nml, sdh, sdh, sdl, zr, zr};
             sc[((wave * RB + rb) * 2 + 0) * 16 + l16] = -rstd * LOG2E;
             sc[((wave * RB + rb) * 2 + 1) * 16 + l16] = mval[rb] * rstd;
         }
     }
-    // Stage 0 landed (at most stage 1's DMA may be outstanding), then publish
-    // it, the correction rows and the scales.
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lds0(DPW));
+    // Stage 0 landed (at most the DMA of stages 1 and 2 may be outstanding),
+    // then publish it, the correction rows and the scales.
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lds0(2 * DPW));
     barrier();
 
     // Weight fragment (B operand) of K-group kg for row l16 of half hf (p or g):
@@ -357,50 +381,152 @@ __global__ __launch_bounds__(256, 2) void k1_project_fold(
         return *reinterpret_cast<const u32x4*>(sl + hf * 32 * D + wb[kg & 3] + 256 * (kg >> 2));
     };
 
-    for (int q = 0; q < NQ; ++q) {
-        if (q + 2 < NQ) issue(q + 2);    // into the slot stage q - 1 used
+    const bool full = mvalid == ROWS;   // wave-uniform: no tail lanes
+    // Each stage runs in two halves of HB = RB / 2 pair blocks.  A half is
+    // NSTEP = KG + 1 steps: the correction K-group, then K-groups 0 .. KG-1.
+    // Step s issues the LDS reads of step s + 1 (the last step those of the
+    // next half's correction step), the half's 2 HB MFMAs of step s and,
+    // alternating with them, the arithmetic of a share of the previous half's
+    // epilogue.  Each step is a scheduling region of its own, so the sigmoid
+    // math runs under the matrix cores instead of after them.
+    constexpr int HB = RB / 2;
+    constexpr int NSTEP = KG + 1;
+    constexpr int NOUT = HB * 4;   // epilogue outputs per lane per half
+    const unsigned char* xfb = xfa + (g4 == 0 ? wave * RB * 256 : NWV * RB * 256) + l16 * 16;
+    // Per-pair scales of this lane's four output pairs in every block (they do
+    // not change from stage to stage).
+    f32x4 cxr[RB], mrr[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        cxr[rb] = *reinterpret_cast<const f32x4*>(sc + ((wave * RB + rb) * 2 + 0) * 16 + 4 * g4);
+        mrr[rb] = *reinterpret_cast<const f32x4*>(sc + ((wave * RB + rb) * 2 + 1) * 16 + 4 * g4);
+    }
+    auto fence = [&]() { __builtin_amdgcn_sched_barrier(0); };
+    // One epilogue output (index k of NOUT) of the half Hp whose accumulators
+    // are pp/gp; writes a block's four pairs to the output tile after its
+    // fourth output.
+    const int oswz = 2 * (l16 >> 1);
+    auto epi_out = [&](auto hpc, int k, const f32x4* pp, const f32x4* gp, f32x4* ov) {
+        constexpr int HP = decltype(hpc)::value;
+        const int j = k / 4, e = k % 4, rb = HP * HB + j;
+        ov[j][e] = mrr[rb][e] * pp[j][e] *
+                   __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(cxr[rb][e] * gp[j][e]));
+        if (e == 3) {
+            bf16x4 h;
+            h[0] = (bf16)ov[j][0]; h[1] = (bf16)ov[j][1]; h[2] = (bf16)ov[j][2]; h[3] = (bf16)ov[j][3];
+            *reinterpret_cast<bf16x4*>(otile + l16 * 128 + (((rb * 4 + g4) ^ oswz) << 3)) = h;
+        }
+    };
+    // Store stage q's output tile: lane L reads the 16 bytes of pairs 8 (L % 8)
+    // .. +7 of channel row L / 8 (+ 8 for the second instruction) and writes
+    // them to the channel-major output, whole 128-byte runs per row.  Runs past
+    // the end go to the sink, so every wave issues exactly two stores.
+    const int orow = lane >> 3, ochk = lane & 7;
+    auto store_tile = [&](int q) {
+        const int part = q < NQ / 2 ? 0 : 1;
+        bf16* base = (part ? b_cm : a_cm) + ((size_t)bidx * C + (q - part * (NQ / 2)) * 16) * NN + cm0;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int r = orow + 8 * i;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(otile + r * 128 + (((2 * ochk) ^ (2 * (r >> 1))) << 3));
+            bf16* p = (full || 8 * ochk < mvalid) ? base + (size_t)r * NN + 8 * ochk : sink + lane * 8;
+            *reinterpret_cast<u32x4*>(p) = v;
+        }
+    };
+    // Operands of a half's correction step: the correction rows of stage q
+    // (B side, every lane the entry of its row) and the z-side correction
+    // fragments of the half's blocks (lane group 0 only; others read zeros).
+    struct Pre { u32x4 b0, b1, xe[HB]; };
+    auto load_corr = [&](auto hc, int q, Pre& pr) {
+        constexpr int H = decltype(hc)::value;
+        pr.b0 = ext[q * 32 + l16];
+        pr.b1 = ext[q * 32 + 16 + l16];
+#pragma unroll
+        for (int j = 0; j < HB; ++j) pr.xe[j] = *reinterpret_cast<const u32x4*>(xfb + (H * HB + j) * 256);
+    };
+    // One half: MFMAs of blocks H of stage q (slot sl) into ap/ag, starting from
+    // the prefetched correction operands in cur; on return cur holds the next
+    // half's (half HN of stage qn).  If EPI, the previous half (HP, stage qp,
+    // accumulators pp/gp) is finished alongside.
+    auto half = [&](auto hc, auto epic, auto hpc, auto hnc, const unsigned char* sl, int q, Pre& cur,
+                    f32x4* ap, f32x4* ag, int qp, const f32x4* pp, const f32x4* gp, int qn) {
+        constexpr int H = decltype(hc)::value;
+        constexpr bool EPI = decltype(epic)::value;
+        f32x4 ov[HB];
+        u32x4 b0 = cur.b0, b1 = cur.b1;
+#pragma unroll
+        for (int st = 0; st < NSTEP; ++st) {
+            // Prefetch the next step's B operands (or the next half's correction step).
+            u32x4 n0, n1;
+            Pre nx;
+            if (st + 1 < NSTEP) {
+                n0 = wfrag(sl, 0, st);
+                n1 = wfrag(sl, 1, st);
+            } else {
+                load_corr(hnc, qn, nx);
+            }
+            // This step's MFMAs, each followed by a share of the epilogue.
+            const int lo = st * NOUT / NSTEP, hi = (st + 1) * NOUT / NSTEP;   // constants after unrolling
+#pragma unroll
+            for (int j = 0; j < HB; ++j) {
+                const u32x4 a = st == 0 ? cur.xe[j] : zf[H * HB + j][st - 1];
+                if (st == 0) {
+                    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+                    ap[j] = Elem<bf16>::mma(a, b0, z4);
+                    ag[j] = Elem<bf16>::mma(a, b1, z4);
+                } else {
+                    ap[j] = Elem<bf16>::mma(a, b0, ap[j]);
+                    ag[j] = Elem<bf16>::mma(a, b1, ag[j]);
+                }
+            }
+            if (EPI) {
+#pragma unroll
+                for (int k = lo; k < hi; ++k) epi_out(hpc, k, pp, gp, ov);
+            }
+            // Alternate MFMAs with the epilogue arithmetic inside the step.
+            __builtin_amdgcn_sched_group_barrier(0x0100, 4, 0);            // LDS reads
+#pragma unroll
+            for (int m = 0; m < 2 * HB; ++m) {
+                __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);        // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x0402, 3, 0);        // VALU / transcendental
+            }
+            fence();
+            if (st + 1 < NSTEP) { b0 = n0; b1 = n1; } else { cur = nx; }
+        }
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using T_ = std::integral_constant<bool, true>;
+    using F_ = std::integral_constant<bool, false>;
+    f32x4 pA[HB], gA[HB], pB[HB], gB[HB];
+    Pre cur;
+    load_corr(I0{}, 0, cur);
+    half(I0{}, F_{}, I1{}, I1{}, ring, 0, cur, pA, gA, 0, pB, gB, 0);
+    for (int q = 0;; ++q) {
         const unsigned char* sl = ring + (q % NSW) * STAGE;
-        f32x4 ap[RB], ag[RB];
-        {
-            const u32x4 ep = g4 == 0 ? ext[q * 32 + l16] : zero;
-            const u32x4 eg = g4 == 0 ? ext[q * 32 + 16 + l16] : zero;
-            const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb) {
-                ap[rb] = Elem<bf16>::mma(zf[rb][KG], ep, z4);
-                ag[rb] = Elem<bf16>::mma(zf[rb][KG], eg, z4);
-            }
-        }
-#pragma unroll
-        for (int kg = 0; kg < KG; ++kg) {
-            const u32x4 wp = wfrag(sl, 0, kg), wg = wfrag(sl, 1, kg);
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb) {
-                ap[rb] = Elem<bf16>::mma(zf[rb][kg], wp, ap[rb]);
-                ag[rb] = Elem<bf16>::mma(zf[rb][kg], wg, ag[rb]);
-            }
-        }
-        // Lane holds channel l16 of the group, pairs rb*16 + 4*g4 + e.
-        const int half = q < NQ / 2 ? 0 : 1;
-        const int ch = (q - half * (NQ / 2)) * 16 + l16;
-        bf16* dst = (half ? b_cm : a_cm) + ((size_t)bidx * C + ch) * NN + cm0;
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-            const f32x4 cx = *reinterpret_cast<const f32x4*>(sc + ((wave * RB + rb) * 2 + 0) * 16 + 4 * g4);
-            const f32x4 mr = *reinterpret_cast<const f32x4*>(sc + ((wave * RB + rb) * 2 + 1) * 16 + 4 * g4);
-            f32x4 o;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                o[e] = mr[e] * ap[rb][e] * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(cx[e] * ag[rb][e]));
-            const int m0 = rb * 16 + 4 * g4;
-            bf16* p = m0 < mvalid ? dst + m0 : sink + lane * 4;
-            Elem<bf16>::store4(p, 0, o);
-        }
-        // Stage q + 1 must have landed: after its DMA this wave issued the
-        // stores of stage q - 1, the DMA of stage q + 2 and the stores of stage q.
-        if (q + 2 < NQ) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lds0(DPW + RB));
-        else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lds0(0));
+        const int qn = q + 1 < NQ ? q + 1 : q;
+        half(I1{}, T_{}, I0{}, I0{}, sl, q, cur, pB, gB, q, pA, gA, qn);
+        if (q + 1 == NQ) break;
+        // Stage q + 1 must have landed.  Every wave issues, in this order per
+        // iteration: the DMA of stage q + 3 (DPW instructions, while q + 3 <
+        // NQ) and the two stores of stage q.  Stage q + 1's DMA was issued in
+        // the prologue (q < 2) or two iterations back, so the operations newer
+        // than it are: stage 2's DMA (q = 0); then stage q + 2's DMA and two
+        // iterations' stores (DPW + 4), of which all but the last DPW + 2 may
+        // be waited for; 4 stores when no DMA was issued in between.
+        if (q == 0) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lds0(DPW));
+        else if (q + 2 < NQ) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lds0(DPW + 2));
+        else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lds0(2));
         barrier();
+        if (q + 3 < NQ) issue(q + 3);    // into the slot stage q used
+        half(I0{}, T_{}, I1{}, I1{}, ring + ((q + 1) % NSW) * STAGE, q + 1, cur, pA, gA, q, pB, gB, q + 1);
+        store_tile(q);                   // the tile is complete; stage q + 1's epilogue starts after
+    }
+    {
+        f32x4 ov[HB];
+#pragma unroll
+        for (int k = 0; k < NOUT; ++k) epi_out(I1{}, k, pB, gB, ov);
+        store_tile(NQ - 1);
     }
 }
 
