@@ -11,6 +11,7 @@ FLOPs counted per call: 2*B*C*N^3 (contraction) + 2*B*N^2*D*(4C + D) (input
 projections incl. the output gate) + 2*B*N^2*C*D (output projection).
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -22,6 +23,32 @@ sys.path.insert(0, ROOT)
 METRIC = "TriMul fwd ms/call + TFLOP/s (% bf16 MFMA peak), B=1 N=4096 D=256"
 PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}   # MI355X dense matrix peaks (published)
 PEAK_HBM_GBS = 8000.0
+# HBM bytes per contraction launch, measured with rocprofv3 counters (see the
+# file for the commands and the copy-kernel calibration); used only while the
+# contraction kernel's sources are the ones the counters were taken on.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k2_contract_hbm_traffic_out_bf16_b1_n4096_d256.json")
+K2_SOURCES = [os.path.join(ROOT, "triangle_multiplication_amd", "csrc", f)
+              for f in ("k2_contract.hip", "trimul_device.hpp")]
+
+
+def k2_source_digest():
+    h = hashlib.sha256()
+    for f in K2_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(name, direction):
+    """Counter-derived HBM bytes per contraction launch, or None if not taken on these sources."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("workload") != name or t.get("direction") != direction or t.get("sources_sha256") != k2_source_digest():
+        return None
+    return float(t["hbm_bytes_per_launch"])
 
 
 def log(*a):
@@ -74,9 +101,17 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--direction", default=None)
     ap.add_argument("--kernel-reps", type=int, default=10)
-    ap.add_argument("--cpu-sample", type=int, default=64)
+    ap.add_argument("--cpu-sample", type=int, default=384,
+                    help="side of the (i, j) grid the oracle computes for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy-gib", type=int, default=0,
+                    help="only run one plain device copy of this many GiB (counter calibration) and exit")
+    ap.add_argument("--print-k2-digest", action="store_true",
+                    help="print the digest of the contraction kernel's sources and exit")
     args = ap.parse_args()
+    if args.print_k2_digest:
+        print(k2_source_digest())
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -85,6 +120,15 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.calibration_copy_gib:
+        n = args.calibration_copy_gib << 30
+        src = torch.zeros(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copied %d bytes" % n)
+        return
     from triangle_multiplication_amd import binding, inputs
 
     name = args.workload or inputs.HEADLINE
@@ -160,7 +204,8 @@ def main():
                    "mask": wl.mask, "flops_per_call": flops},
         "pct_peak": round(100.0 * value / peak, 2),
         "roofline": {"bound": "mfma", "achieved": round(k2_tf, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(k2_tf / peak, 4), "traffic": None, "kernel": "k2_contract",
+                     "frac": round(k2_tf / peak, 4), "traffic": measured_traffic(name, direction),
+                     "kernel": "k2_contract",
                      "per_launch": "2*B*C*N^3 = %.4g FLOP" % k2_flops, "avg_ms": round(k2_ms, 4)},
         "kernels": {
             "k1_project": {"ms": round(k1_ms, 4), "tflops": round(k1_flops / k1_ms / 1e9, 2),
