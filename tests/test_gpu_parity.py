@@ -164,6 +164,24 @@ def test_fwd_small_shapes(tb, dtype, direction, B, N, D, C, masked):
     assert err <= TOL[dtype]
 
 
+@pytest.mark.parametrize("direction", ["outgoing", "incoming"])
+@pytest.mark.parametrize("D", [128, 256])
+@pytest.mark.parametrize("mean", [3.0, -8.0])
+def test_fwd_shifted_mean(tb, direction, D, mean):
+    """z rows whose mean is several standard deviations from zero: the bf16
+    kernels apply LayerNorm algebraically with one-pass statistics, which must
+    stay within tolerance there too."""
+    B, N, C = 1, 40, D
+    say("fwd shifted mean", direction, D, mean)
+    w = inputs.make_weights(D, C, "bf16", random_ln=True)
+    z = (inputs.make_z(B, N, D, "fp32") + mean).to(torch.bfloat16)
+    layer = _layer(tb, w, "bf16")
+    out = layer.forward(z.cuda(), None, direction)
+    err = oracle_check(z, None, w, direction, out, full=True)
+    say("  err", err)
+    assert err <= TOL["bf16"]
+
+
 WL = inputs.WORKLOADS
 
 
