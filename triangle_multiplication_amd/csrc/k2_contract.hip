@@ -211,7 +211,7 @@ __global__ __launch_bounds__(512) void k2_contract_pp(const bf16* __restrict__ A
     const unsigned logical = (g & 7u) * (total >> 3) + (g >> 3);
     const size_t bc = logical / per_bc;
     const int t = (int)(logical % per_bc);
-    constexpr int GM = 4;
+    constexpr int GM = 8;   // row panels per group (measured: 8 beats 1, 2, 4 and 16 at N = 4096)
     const int first_i = (t / (GM * tiles)) * GM;
     const int gm = min(GM, tiles - first_i);
     const int ti = first_i + (t % (GM * tiles)) % gm;
