@@ -246,7 +246,10 @@ struct Cfg {
     static constexpr int SLOT = ZB + OB;
     static constexpr int ZDMA = ZB / 1024, DMA_ALL = (ZB + OB) / 1024;
     static constexpr int DPW = DMA_ALL / NW;                  // 1 KB DMA instructions per wave per tile
-    static constexpr int STORES = NB * RBW;                   // global stores per wave per tile
+    // With two row blocks per wave they are interleaved so that each lane's
+    // eight results are eight consecutive channels (one 16-byte store).
+    static constexpr bool PAIRED = RBW == 2;
+    static constexpr int STORES = PAIRED ? NB : NB * RBW;     // global stores per wave per tile
     static constexpr int FRAG = 1024;                         // one extra K-group fragment
     static constexpr int STAT = 4 * FRAG + 4 * 64;            // [kind][block] fragments + scales
     static constexpr int LDS = NS * SLOT + 2 * STAT;
@@ -290,7 +293,9 @@ __global__ __launch_bounds__(512) void k3_output_fold(
     u32x4 xg[RBW], xp[RBW];
 #pragma unroll
     for (int r = 0; r < RBW; ++r) {
-        const int d = (wave + r * NW) * 16 + l16;
+        // Output channel of MFMA row l16 of block r: with paired blocks, rows
+        // 4k + e of block r give channel 32 wave + 8k + 4r + e.
+        const int d = Cf::PAIRED ? 32 * wave + 8 * (l16 >> 2) + 4 * r + (l16 & 3) : (wave + r * NW) * 16 + l16;
 #pragma unroll
         for (int kg = 0; kg < KGD; ++kg) wg[r][kg] = ld16(Wg + (size_t)d * D + (kg * 4 + g4) * 8);
 #pragma unroll
@@ -432,14 +437,26 @@ __global__ __launch_bounds__(512) void k3_output_fold(
             }
             const float cx = *reinterpret_cast<const float*>(st + 4 * FRAG + bb * 64 + l16 * 4);
             const float ro = *reinterpret_cast<const float*>(st + 4 * FRAG + (NB + bb) * 64 + l16 * 4);
-            // Lane holds output channels rb*16 + 4*g4 + 0..3 of pair 16*bb + l16.
+            // Lane holds, for pair 16*bb + l16, output channels 32 wave + 8 g4 +
+            // 4r + e (paired blocks) or (wave + 8r)*16 + 4 g4 + e.
+            if constexpr (Cf::PAIRED) {
+                bf16x8 h;
 #pragma unroll
-            for (int r = 0; r < RBW; ++r) {
-                f32x4 res;
+                for (int r = 0; r < 2; ++r)
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    res[e] = ro * ay[r][e] * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(cx * ag[r][e]));
-                Elem<bf16>::store4(ob, (size_t)(bb * 16 + l16) * D + (wave + r * NW) * 16 + 4 * g4, res);
+                    for (int e = 0; e < 4; ++e)
+                        h[4 * r + e] = (bf16)(ro * ay[r][e] *
+                                              __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(cx * ag[r][e])));
+                *reinterpret_cast<bf16x8*>(ob + (size_t)(bb * 16 + l16) * D + 32 * wave + 8 * g4) = h;
+            } else {
+#pragma unroll
+                for (int r = 0; r < RBW; ++r) {
+                    f32x4 res;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        res[e] = ro * ay[r][e] * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(cx * ag[r][e]));
+                    Elem<bf16>::store4(ob, (size_t)(bb * 16 + l16) * D + (wave + r * NW) * 16 + 4 * g4, res);
+                }
             }
         }
     };
