@@ -303,6 +303,166 @@ __global__ __launch_bounds__(512) void k2_contract_pp(const bf16* __restrict__ A
     }
 }
 
+// Persistent form of k2_contract_pp: one workgroup per CU walks its tiles
+// g, g + G, ... (the same XCD-banded tile order), and the step sequence runs
+// on across tile boundaries -- the DMA ring is never drained, so the next
+// tile's first steps are in flight while the current one finishes, and a
+// tile's stores overlap the next tile's multiplies.  Each workgroup starts its
+// K loop at its own offset (the sum's order does not matter), which spreads
+// the tile boundaries, and so the store bursts, over time.  A wave stores its
+// block and clears its accumulators right after the compute phase of a
+// tile's last step; both groups do this at the same point of their own phase
+// sequence, so every wave still executes the same barriers.
+template <int NSP>
+__global__ __launch_bounds__(512) void k2_contract_ppp(const bf16* __restrict__ A,
+                                                       const bf16* __restrict__ Bm,
+                                                       bf16* __restrict__ O, int N, int total)
+{
+    using namespace k2big;
+    constexpr int NW = 8;
+    constexpr int DPO = OPB / 1024 / NW;            // DMA instructions per wave per operand (2)
+    constexpr int DPS = 2 * DPO;                    // per wave per step
+    constexpr int DIST = NSP - 1;                   // DMA runs this many steps ahead
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[NSP * STB];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 2, wn = wave & 3;        // group = wm
+    const size_t slab = (size_t)N * N;
+    const int tiles = (N + BM - 1) / BM;
+    const int per_bc = tiles * tiles;
+    const int G = gridDim.x, g = blockIdx.x;
+    const int n_my = (total - g + G - 1) / G;       // tiles of this workgroup (g < total)
+    const int nk = (N + BK - 1) / BK;
+    const int koff = 0;   // rotating the K loop per workgroup loses the L2 sharing of K-slices
+    const int S = n_my * nk;                        // steps of this workgroup (< 2^31)
+
+    // Tile tl of this workgroup: virtual block g + tl*G through the XCD-banded
+    // order (total and G are multiples of 8, so the band is g's).
+    auto tile_geo = [&](int tl, size_t& bc, int& i0, int& j0) {
+        const unsigned vb = (unsigned)g + (unsigned)tl * (unsigned)G;
+        const unsigned logical = (vb & 7u) * ((unsigned)total >> 3) + (vb >> 3);
+        bc = logical / per_bc;
+        const int t = (int)(logical % per_bc);
+        constexpr int GM = 8;
+        const int first_i = (t / (GM * tiles)) * GM;
+        const int gm = min(GM, tiles - first_i);
+        i0 = (first_i + (t % (GM * tiles)) % gm) * BM;
+        j0 = ((t % (GM * tiles)) / gm) * BN;
+    };
+
+    const unsigned nrec = (unsigned)(slab * sizeof(bf16));
+    const int dpos = (lane & 7) ^ (lane >> 3);
+    const int dr = 2 * (lane >> 3) + (dpos >> 2), dc = dpos & 3;
+    const unsigned qstride = (unsigned)N * 32u;
+    const unsigned lane_off = (unsigned)(wave * 16 * DPO + dr) * (unsigned)N * 2u + dc * 16u;
+
+    // DMA cursor: the next step to load is K-step ikk of tile itl.  The tile's
+    // buffer descriptors and row offsets are recomputed only when the cursor
+    // enters a new tile; past the workgroup's last tile (and for K-chunks past
+    // N) the offset is pushed beyond the buffer's range, so the DMA reads zeros.
+    int itl = 0, ikk = koff;
+    __amdgpu_buffer_rsrc_t ra, rb;
+    unsigned oa_t = 0, ob_t = 0;
+    bool ilive = true;
+    auto set_tile = [&]() {
+        ilive = itl < n_my;
+        size_t bc; int i0, j0;
+        tile_geo(ilive ? itl : 0, bc, i0, j0);
+        ra = __builtin_amdgcn_make_buffer_rsrc((void*)(A + bc * slab), 0, nrec, 0x00020000);
+        rb = __builtin_amdgcn_make_buffer_rsrc((void*)(Bm + bc * slab), 0, nrec, 0x00020000);
+        oa_t = lane_off + (unsigned)i0 * (unsigned)N * 2u;
+        ob_t = lane_off + (unsigned)j0 * (unsigned)N * 2u;
+    };
+    set_tile();
+    int isl = 0;                                    // ring slot of the next step
+    auto issue = [&]() {
+        unsigned char* st = smem + isl * STB + wave * DPO * 1024;
+        const int k0 = ikk * BK;
+        const unsigned kb = (unsigned)k0 * 2u;
+        const unsigned kpen = (ilive && k0 + dc * 8 < N) ? 0u : 0x80000000u;
+#pragma unroll
+        for (int q = 0; q < DPO; ++q) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, TRIMUL_LDS_PTR(st + q * 1024), 16,
+                                                     (oa_t + q * qstride + kb) | kpen, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, TRIMUL_LDS_PTR(st + OPB + q * 1024), 16,
+                                                     (ob_t + q * qstride + kb) | kpen, 0, 0, 0);
+        }
+        if (++isl == NSP) isl = 0;
+        if (++ikk == nk) ikk = 0;
+        if (ikk == koff) { ++itl; set_tile(); }
+    };
+
+    const int rchunk = lane >> 4;
+    const int fa_base = slot_off(wm * 128 + (lane & 15), rchunk);
+    const int fb_base = OPB + slot_off(wn * 64 + (lane & 15), rchunk);
+
+    f32x4 acc[8][4];
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int n = 0; n < 4; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    u32x4 fa[8], fb[4];
+    auto barrier = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+#pragma unroll
+    for (int s0 = 0; s0 < DIST; ++s0) issue();
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm((DIST - 1) * DPS));   // own share of step 0 landed
+    barrier();                                          // ... everyone's
+    if (wm == 1) barrier();                             // group 1 starts one phase late
+
+    int kin = 0;                                        // step within the current tile
+    int tl = 0;
+    int rsl = 0;                                        // ring slot of step s
+    for (int s = 0; s < S; ++s) {
+        // M_s
+        const unsigned char* st = smem + rsl * STB;
+        if (++rsl == NSP) rsl = 0;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) fa[m] = *reinterpret_cast<const u32x4*>(st + fa_base + m * 1024);
+#pragma unroll
+        for (int n = 0; n < 4; ++n) fb[n] = *reinterpret_cast<const u32x4*>(st + fb_base + n * 1024);
+        issue();                                        // step s + DIST
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lds0((DIST - 1) * DPS));
+        barrier();
+        // C_s.  Operands swapped (b rows as the MFMA's A): each lane's four
+        // results are four consecutive j of one i.
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+            for (int n = 0; n < 4; ++n) acc[m][n] = Elem<bf16>::mma(fb[n], fa[m], acc[m][n]);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm((DIST - 1) * DPS));
+        barrier();
+        if (++kin == nk) {
+            // Tile tl complete: store this wave's block and start the next.
+            size_t bc; int i0, j0;
+            tile_geo(tl, bc, i0, j0);
+            bf16* Ob = O + bc * slab;
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const int i = i0 + wm * 128 + m * 16 + (lane & 15);
+#pragma unroll
+                for (int n = 0; n < 4; ++n) {
+                    const int j = j0 + wn * 64 + n * 16 + 4 * (lane >> 4);
+                    if (i < N && j < N) Elem<bf16>::store4(Ob, (size_t)i * N + j, acc[m][n]);
+                    acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+            kin = 0;
+            ++tl;
+        }
+    }
+    if (wm == 0) barrier();                             // balance group 1's extra barrier
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));          // no DMA may outlive the workgroup
+}
+
 template <typename T, int BM, int BN>
 static hipError_t launch_k2(const void* a, const void* b, int B, int C, int N, void* o,
                             hipStream_t s)
@@ -322,8 +482,18 @@ hipError_t launch_contract(const Params& p, const void* a_cm, const void* b_cm, 
     if (p.dtype == DType::BF16 && big) {
         const int tiles = (N + k2big::BM - 1) / k2big::BM;
         dim3 grid((unsigned)((size_t)tiles * tiles * B * p.C));
+#ifdef TRIMUL_K2_NONPERSISTENT
         hipLaunchKernelGGL(k2_contract_pp<4>, grid, dim3(512), 0, s, (const bf16*)a_cm,
                            (const bf16*)b_cm, (bf16*)o, N);
+#else
+        const long long total = (long long)tiles * tiles * B * p.C;
+        int dev = 0, cus = 256;
+        if (hipGetDevice(&dev) == hipSuccess)
+            (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        const long long pg = total < cus ? total : cus;
+        hipLaunchKernelGGL(k2_contract_ppp<4>, dim3((unsigned)pg), dim3(512), 0, s, (const bf16*)a_cm,
+                           (const bf16*)b_cm, (bf16*)o, N, (int)total);
+#endif
         return hipGetLastError();
     }
     if (p.dtype == DType::BF16) return launch_k2<bf16, 128, 128>(a_cm, b_cm, B, p.C, N, o, s);
