@@ -174,11 +174,15 @@ def main():
     B, N, D, C = wl.B, wl.N, wl.D, wl.C
     es = 2 if wl.dtype == "bf16" else 4
     NN = N * N
-    slab = (B * C * NN * es + 255) // 256 * 256
+    ab_shape = binding.ab_storage_shape(wl.dtype, B, C, N)
+    ab_bytes = es
+    for n in ab_shape:
+        ab_bytes *= n
+    ab_slab = (ab_bytes + 255) // 256 * 256
     tdt = inputs.TORCH_DTYPES[wl.dtype]
-    a_cm = ws[:B * C * NN * es].view(tdt).view(B, C, N, N)
-    b_cm = ws[slab:slab + B * C * NN * es].view(tdt).view(B, C, N, N)
-    o_cm = ws[2 * slab:2 * slab + B * C * NN * es].view(tdt).view(B, C, N, N)
+    a_cm = ws[:ab_bytes].view(tdt).view(ab_shape)
+    b_cm = ws[ab_slab:ab_slab + ab_bytes].view(tdt).view(ab_shape)
+    o_cm = ws[2 * ab_slab:2 * ab_slab + B * C * NN * es].view(tdt).view(B, C, N, N)
     reps = args.kernel_reps
     k1_ms = _events_ms(lambda: binding.trimul_internal_project(layer.h, z, mask, direction, a_cm, b_cm), reps)
     k2_ms = _events_ms(lambda: binding.trimul_internal_contract(layer.h, a_cm, b_cm, o_cm), reps)

@@ -87,7 +87,9 @@ trimul_status trimul_create(int D, int C, trimul_dtype dtype, const trimul_weigh
 void trimul_destroy(trimul_handle *h);
 
 /* Bytes of workspace trimul_fwd needs for (B, N): the gated projections a and
- * b and the contraction o, each [B][C][N][N] in the dtype, 256-byte aligned. */
+ * b, each B*C*N*Kp elements of the dtype (Kp = N rounded up to a multiple of
+ * 32 for bf16, Kp = N for fp32), and the contraction o, B*C*N*N elements; each
+ * of the three rounded up to 256 bytes. */
 trimul_status trimul_workspace_size(const trimul_handle *h, int B, int N, size_t *bytes);
 
 /* Same figure from the widths alone (host arithmetic only; no device needed). */

@@ -19,10 +19,15 @@ extern "C" {
 /*
  * LayerNorm_in, gated input projection and mask (the first three lines of the
  * formula in trimul.h), stored channel-major for the contraction:
- *   outgoing: a_cm[b][c][i][k] = a_(b,i,k,c),  b_cm[b][c][j][k] = b_(b,j,k,c)
- *   incoming: a_cm[b][c][i][k] = a_(b,k,i,c),  b_cm[b][c][j][k] = b_(b,k,j,c)
- * so that the contraction is always o[b][c][i][j] = sum_k a_cm[..i,k] b_cm[..j,k].
- * a_cm, b_cm: [B][C][N][N], 16-byte aligned.
+ *   outgoing: A[b][c](i, k) = a_(b,i,k,c),  B[b][c](j, k) = b_(b,j,k,c)
+ *   incoming: A[b][c](i, k) = a_(b,k,i,c),  B[b][c](j, k) = b_(b,k,j,c)
+ * so that the contraction is always o[b][c][i][j] = sum_k A(i, k) B(j, k).
+ * Storage of one (b, c) slab of A or B (a_cm, b_cm are [B][C][slab]):
+ *   fp32 handles: plain, element (r, k) at r * N + k (slab N * N);
+ *   bf16 handles: K-blocked, element (r, k) at ((k / 32) * N + r) * 32 + k % 32
+ *                 (slab N * Kp, Kp = N rounded up to 32; entries with k >= N
+ *                 are padding, never written or read).
+ * a_cm, b_cm: 16-byte aligned.
  */
 trimul_status trimul_internal_project(trimul_handle *h, const void *z, const void *pair_mask,
                                       int B, int N, trimul_direction dir, void *a_cm, void *b_cm,
@@ -30,8 +35,9 @@ trimul_status trimul_internal_project(trimul_handle *h, const void *z, const voi
 
 /*
  * Triangle contraction, C*B independent N x N x N products with fp32
- * accumulation: o[b][c][i][j] = sum_k a_cm[b][c][i][k] * b_cm[b][c][j][k],
- * rounded once to the dtype.  o: [B][C][N][N].
+ * accumulation: o[b][c][i][j] = sum_k A[b][c](i, k) * B[b][c](j, k), rounded
+ * once to the dtype.  a_cm, b_cm in the storage described above; o: plain
+ * [B][C][N][N].
  */
 trimul_status trimul_internal_contract(trimul_handle *h, const void *a_cm, const void *b_cm,
                                        int B, int N, void *o, hipStream_t stream);

@@ -60,13 +60,25 @@ def test_arch_gate_null():
 
 
 def test_workspace_query_sizes():
-    # a, b and o, each [B][C][N][N], 256-byte aligned
+    # a and b: B*C*N*Kp elements (bf16: Kp = N rounded up to 32; fp32: Kp = N),
+    # o: B*C*N*N elements; each rounded up to 256 bytes
+    def r256(x):
+        return (x + 255) // 256 * 256
     assert tb.trimul_workspace_query(256, 256, "bf16", 1, 4096) == 3 * 256 * 4096 * 4096 * 2
     assert tb.trimul_workspace_query(32, 32, "fp32", 1, 64) == 3 * 32 * 64 * 64 * 4
     n = tb.trimul_workspace_query(32, 64, "bf16", 3, 8)
-    slab = 3 * 64 * 8 * 8 * 2
-    assert n == 3 * ((slab + 255) // 256 * 256)
+    assert n == 2 * r256(3 * 64 * 8 * 32 * 2) + r256(3 * 64 * 8 * 8 * 2)
+    n = tb.trimul_workspace_query(64, 32, "bf16", 2, 200)
+    assert n == 2 * r256(2 * 32 * 200 * 224 * 2) + r256(2 * 32 * 200 * 200 * 2)
+    n = tb.trimul_workspace_query(64, 32, "fp32", 2, 200)
+    assert n == 3 * r256(2 * 32 * 200 * 200 * 4)
     assert tb.trimul_workspace_query(128, 128, "bf16", 1, 8192) == 3 * 128 * 8192 ** 2 * 2
+
+
+def test_ab_storage_shape():
+    assert tb.ab_storage_shape("bf16", 2, 64, 200) == (2, 64, 7, 200, 32)
+    assert tb.ab_storage_shape("bf16", 1, 32, 4096) == (1, 32, 128, 4096, 32)
+    assert tb.ab_storage_shape("fp32", 2, 64, 200) == (2, 64, 200, 200)
 
 
 @pytest.mark.parametrize("D,C", [(48, 32), (32, 0), (288, 32), (32, 300), (16, 16)])

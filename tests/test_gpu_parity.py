@@ -40,6 +40,27 @@ def _layer(tb, w, dtype):
     return tb.TriMul(w, dtype)
 
 
+def _to_ab_storage(x, dtype):
+    """Plain [B, C, N, N] (row, k) tensor -> the stage buffers' storage
+    (include/trimul_internal.h): bf16 K-blocked [B, C, Kp/32, N, 32] with the
+    k >= N padding filled with NaN (never read), fp32 unchanged."""
+    if dtype != "bf16":
+        return x.contiguous()
+    B, C, N, _ = x.shape
+    kp = (N + 31) // 32 * 32
+    xp = torch.full((B, C, N, kp), float("nan"), dtype=x.dtype, device=x.device)
+    xp[..., :N] = x
+    return xp.view(B, C, N, kp // 32, 32).permute(0, 1, 3, 2, 4).contiguous()
+
+
+def _from_ab_storage(x, dtype):
+    """Inverse of _to_ab_storage: storage -> plain [B, C, N, N]."""
+    if dtype != "bf16":
+        return x
+    B, C, nb, N, _ = x.shape
+    return x.permute(0, 1, 3, 2, 4).reshape(B, C, N, nb * 32)[..., :N]
+
+
 def _exact_contract_reference(a, b, rows=None, chans=None):
     """RNE-rounded exact integer sums sum_k a[c,i,k] b[c,j,k] in float64 on the device."""
     A = a if chans is None else a[:, chans]
@@ -54,7 +75,8 @@ def _exact_contract_reference(a, b, rows=None, chans=None):
 # Contraction kernel alone: exact on small integers (bitwise)
 # ----------------------------------------------------------------------------
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
-@pytest.mark.parametrize("B,C,N", [(1, 32, 8), (2, 32, 200), (1, 64, 136), (1, 32, 384)])
+@pytest.mark.parametrize("B,C,N", [(1, 32, 8), (2, 32, 200), (1, 64, 136), (1, 32, 384),
+                                   (1, 32, 2056)])
 def test_contract_exact_integers(tb, dtype, B, C, N):
     say("contract exact", dtype, B, C, N)
     w = inputs.make_weights(C, C, dtype)
@@ -63,7 +85,7 @@ def test_contract_exact_integers(tb, dtype, B, C, N):
     tdt = inputs.TORCH_DTYPES[dtype]
     a = torch.randint(-3, 4, (B, C, N, N), generator=g, device="cuda").to(tdt)
     b = torch.randint(-3, 4, (B, C, N, N), generator=g, device="cuda").to(tdt)
-    o = layer.contract(a, b)
+    o = layer.contract(_to_ab_storage(a, dtype), _to_ab_storage(b, dtype))
     ref = _exact_contract_reference(a, b).to(tdt)
     torch.cuda.synchronize()
     assert torch.equal(o, ref)
@@ -78,7 +100,7 @@ def test_contract_exact_integers_full_size(tb, C, N):
     g = torch.Generator(device="cuda").manual_seed(8)
     a = torch.randint(-3, 4, (1, C, N, N), generator=g, device="cuda", dtype=torch.int8).to(torch.bfloat16)
     b = torch.randint(-3, 4, (1, C, N, N), generator=g, device="cuda", dtype=torch.int8).to(torch.bfloat16)
-    o = layer.contract(a, b)
+    o = layer.contract(_to_ab_storage(a, "bf16"), _to_ab_storage(b, "bf16"))
     I, _ = inputs.sample_grid(N, 64)
     rows = torch.as_tensor(I, device="cuda")
     chans = torch.as_tensor([0, 1, C // 2 + 3, C - 1], device="cuda")
@@ -105,6 +127,7 @@ def test_project_stage(tb, dtype, direction, B, N, D, C):
     ref = oracle.trimul_full(z.float().numpy(), mask.float().numpy(), w, direction, dumps=True)
     layer = _layer(tb, w, dtype)
     a, b = layer.project(z.cuda(), mask.cuda(), direction)
+    a, b = _from_ab_storage(a, dtype), _from_ab_storage(b, dtype)
     a, b = a.float().cpu().numpy(), b.float().cpu().numpy()
     ra, rb = ref["a"], ref["b"]  # [B, N, N, C] pair layout
     if direction == "outgoing":

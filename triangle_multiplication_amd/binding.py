@@ -152,8 +152,17 @@ def trimul_internal_project(h, z, mask, direction, a_cm, b_cm, stream=None):
                                         _ptr(a_cm), _ptr(b_cm), _stream(stream)))
 
 
+def ab_storage_shape(dtype, B, C, N):
+    """Tensor shape of the stage buffers a_cm, b_cm (include/trimul_internal.h):
+    bf16 is K-blocked, [B][C][Kp/32][N][32] with Kp = N rounded up to 32;
+    fp32 is plain [B][C][N][N]."""
+    if dtype == "bf16":
+        return (B, C, (N + 31) // 32, N, 32)
+    return (B, C, N, N)
+
+
 def trimul_internal_contract(h, a_cm, b_cm, o, stream=None):
-    B, N = int(a_cm.shape[0]), int(a_cm.shape[2])
+    B, N = int(o.shape[0]), int(o.shape[2])
     _check(_lib.trimul_internal_contract(h, _ptr(a_cm), _ptr(b_cm), B, N, _ptr(o),
                                          _stream(stream)))
 
@@ -210,14 +219,15 @@ class TriMul:
     def project(self, z, mask=None, direction="outgoing"):
         import torch
         B, N = int(z.shape[0]), int(z.shape[1])
-        a = torch.empty((B, self.C, N, N), dtype=self.tdtype, device=z.device)
+        a = torch.empty(ab_storage_shape(self.dtype, B, self.C, N), dtype=self.tdtype, device=z.device)
         b = torch.empty_like(a)
         trimul_internal_project(self.h, z, mask, direction, a, b)
         return a, b
 
     def contract(self, a_cm, b_cm):
         import torch
-        o = torch.empty_like(a_cm)
+        B, N = int(a_cm.shape[0]), int(a_cm.shape[-2])
+        o = torch.empty((B, self.C, N, N), dtype=self.tdtype, device=a_cm.device)
         trimul_internal_contract(self.h, a_cm, b_cm, o)
         return o
 

@@ -4,10 +4,11 @@
 //   a_c = m_rs * (p_in x)_c     * sg((g_in x)_c),
 //   b_c = m_rs * (p_in x)_(C+c) * sg((g_in x)_(C+c)),
 // stored channel-major so that the contraction reads k-contiguous rows:
-//   outgoing: pair (r, s) = (i, k) lands at a_cm[c][r*N + s]
-//   incoming: pair (r, s) = (k, i) lands at a_cm[c][s*N + r]
+//   outgoing: pair (r, s) = (i, k) lands at row r, position s of channel c
+//   incoming: pair (r, s) = (k, i) lands at row s, position r of channel c
 // (the single-GPU form of the layout change the fold-cp-ops README performs
-// between its two GEMMs).
+// between its two GEMMs).  fp32 rows are plain ([c][row][k]); bf16 rows are
+// K-blocked ([c][k / 32][row][k % 32], kblk_off).
 //
 // Work split: a 256-thread workgroup is 4 waves; each wave owns ROWS pairs
 // that are consecutive in the channel-major order (outgoing: consecutive s of
@@ -71,6 +72,22 @@ __global__ __launch_bounds__(256) void k1_project(
     }
 
     for (int d = tid; d < D; d += 256) { s_w[d] = ln_w[d]; s_b[d] = ln_b[d]; }
+
+    // Offset within a channel slab of the four pairs this lane stores for
+    // block rb (rows m0 .. m0 + 3 share a row of the slab: 4 divides N).
+    constexpr DType TD = sizeof(T) == 2 ? DType::BF16 : DType::FP32;
+    const size_t slab_ab = ab_slab_elems(TD, N);
+    size_t spos[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        const size_t pos = cm0 + rb * 16 + 4 * (lane >> 4);
+        if constexpr (TD == DType::BF16) {
+            const uint32_t row = (uint32_t)(pos / (size_t)N), k = (uint32_t)(pos - (size_t)row * N);
+            spos[rb] = kblk_off(row, k, (uint32_t)N);
+        } else {
+            spos[rb] = pos;
+        }
+    }
 
     // Weight stage 0 in flight while z is loaded and normalised.
     u32x4 wr[W_LD];
@@ -174,7 +191,7 @@ __global__ __launch_bounds__(256) void k1_project(
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int ch = gq * 32 + h * 16 + (lane & 15);
-            T* dc = dst + ((size_t)bidx * C + ch) * NN + cm0;
+            T* dc = dst + ((size_t)bidx * C + ch) * slab_ab;
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) {
                 const int m0 = rb * 16 + 4 * (lane >> 4);
@@ -182,7 +199,7 @@ __global__ __launch_bounds__(256) void k1_project(
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     o[r] = mv[rb][r] * acc[rb][2 * h][r] * sigmoidf_(acc[rb][2 * h + 1][r]);
-                if (m0 < mvalid) Elem<T>::store4(dc, (size_t)m0, o);
+                if (m0 < mvalid) Elem<T>::store4(dc, spos[rb], o);
             }
         }
         if (q + 1 < nq) wstore(buf ^ 1);
@@ -203,14 +220,16 @@ __global__ __launch_bounds__(256) void k1_project(
 // normalised explicitly.  Statistics take one pass with v_dot2_f32_bf16.
 // Epilogue per output: a = (m rstd acc_p) / (1 + 2^(-log2(e) rstd acc_g)).
 //
-// A workgroup is 4 waves of 64 pairs (geometry as in k1_project); two
-// workgroups share a CU, so one's epilogue overlaps the other's MFMAs.  The
-// weights stream through a 3-slot LDS ring by global->LDS DMA, one 32-row stage
-// ((p, g) rows of 16 channels) at a time, two stages ahead; rows are 2D bytes
-// with 16-byte chunk c of row r stored at c ^ (r % 16).  Each lane's results
-// are four consecutive pairs of one channel, stored as one 8-byte run; lanes
-// of pairs past the end store to a sink so that every wave issues the same
-// number of stores per stage (the DMA waits count them).
+// A workgroup is 4 waves of 64 pairs; a wave's pairs are two adjacent rows of
+// the K-blocked a and b times one 32-wide k block, so each channel's 64 results
+// are one whole 128-byte line.  Two workgroups share a CU, so one's epilogue
+// overlaps the other's MFMAs.  The weights stream through a 3-slot LDS ring by
+// global->LDS DMA, one 32-row stage ((p, g) rows of 16 channels) at a time, two
+// stages ahead; rows are 2D bytes with 16-byte chunk c of row r stored at
+// c ^ (r % 16).  A stage's results go through a per-wave LDS tile and leave as
+// 16-byte stores of whole lines; lanes of pairs past the end store to a sink
+// so that every wave issues the same number of stores per stage (the DMA
+// waits count them).
 // ---------------------------------------------------------------------------
 namespace k1f {
 constexpr int RB = 4, ROWS = RB * 16, NWV = 4, NSW = 3, CMAX = 256;
@@ -264,20 +283,21 @@ __global__ __launch_bounds__(256, 2) void k1_project_fold(
     const int t = blockIdx.x % blocks_per_b;
     const int NQ = C / 8;   // stages: C/16 channel groups of a, then of b
 
-    // Pair geometry: row m <-> z pair zbase + m * zstride, channel-major position cm0 + m.
-    size_t zbase, zstride, cm0;
-    int mvalid;
-    if (!incoming) {
-        const size_t p0 = ((size_t)t * NWV + wave) * ROWS;
-        zbase = p0; zstride = 1; cm0 = p0;
-        mvalid = p0 < NN ? (int)min((size_t)ROWS, NN - p0) : 0;
-    } else {
-        const int rtiles = (N + ROWS - 1) / ROWS;
-        const int rt = t % rtiles, st = t / rtiles;
-        const int r0 = rt * ROWS, s = st * NWV + wave;
-        zbase = (size_t)r0 * N + s; zstride = (size_t)N; cm0 = (size_t)s * N + r0;
-        mvalid = min(ROWS, N - r0);
-    }
+    // Pair geometry.  A wave owns 64 pairs that fill whole 128-byte lines of
+    // the K-blocked a and b: storage rows row0 and row0 + 1 (row0 even) times
+    // the 32-wide k block [k0, k0 + 32).  MFMA row m is the pair at storage row
+    // row0 + m / 32, k = k0 + m % 32; pairs with k >= N do not exist (only k
+    // below k0 + kvalid does).
+    //   outgoing: storage row i = z row, k = z column: z pair (row, k)
+    //   incoming: storage row i = z column, k = z row: z pair (k, row)
+    const int nkb = (N + 31) / 32;
+    const int unit = t * NWV + wave;
+    const int row0 = 2 * (unit / nkb), k0 = 32 * (unit % nkb);
+    const int kvalid = row0 < N ? min(32, N - k0) : 0;   // the last workgroup may hold idle waves
+    auto zpair = [&](int m) -> size_t {
+        const size_t row = (size_t)(row0 + (m >> 5)), k = (size_t)(k0 + (m & 31));
+        return incoming ? k * N + row : row * N + k;
+    };
 
     // Per-lane source offsets (elements) of this wave's DMA instructions within
     // a stage: instruction qi = wave + 4 i fills bytes [qi KB, qi KB + 1 KB) of
@@ -327,16 +347,16 @@ __global__ __launch_bounds__(256, 2) void k1_project_fold(
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         const int m = rb * 16 + l16;
-        const bf16* zp = zb + (zbase + (size_t)m * zstride) * D;
+        const bool live = (m & 31) < kvalid;
+        const bf16* zp = zb + (live ? zpair(m) : 0) * D;
 #pragma unroll
-        for (int kg = 0; kg < KG; ++kg) zf[rb][kg] = (m < mvalid) ? ld16(zp + (kg * 4 + g4) * 8) : zero;
+        for (int kg = 0; kg < KG; ++kg) zf[rb][kg] = live ? ld16(zp + (kg * 4 + g4) * 8) : zero;
     }
     float mval[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         const int m = rb * 16 + l16;
-        mval[rb] = m < mvalid ? (mask ? (float)mask[(size_t)bidx * NN + zbase + (size_t)m * zstride] : 1.0f)
-                              : 0.0f;
+        mval[rb] = (m & 31) < kvalid ? (mask ? (float)mask[(size_t)bidx * NN + zpair(m)] : 1.0f) : 0.0f;
     }
     const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
@@ -381,7 +401,7 @@ __global__ __launch_bounds__(256, 2) void k1_project_fold(
         return *reinterpret_cast<const u32x4*>(sl + hf * 32 * D + wb[kg & 3] + 256 * (kg >> 2));
     };
 
-    const bool full = mvalid == ROWS;   // wave-uniform: no tail lanes
+    const bool full = kvalid == 32;   // wave-uniform: no tail lanes
     // Each stage runs in two halves of HB = RB / 2 pair blocks.  A half is
     // NSTEP = KG + 1 steps: the correction K-group, then K-groups 0 .. KG-1.
     // Step s issues the LDS reads of step s + 1 (the last step those of the
@@ -421,15 +441,20 @@ __global__ __launch_bounds__(256, 2) void k1_project_fold(
     // .. +7 of channel row L / 8 (+ 8 for the second instruction) and writes
     // them to the channel-major output, whole 128-byte runs per row.  Runs past
     // the end go to the sink, so every wave issues exactly two stores.
+    // A channel's 64 pairs are one 128-byte line of the K-blocked storage
+    // (rows row0, row0 + 1 of block k0 / 32), in MFMA row order.
     const int orow = lane >> 3, ochk = lane & 7;
+    const size_t slab_ab = ab_slab_elems(DType::BF16, N);
+    const uint32_t spos = kblk_off((uint32_t)row0, (uint32_t)k0, (uint32_t)N) + 8 * ochk;
+    const bool olive = 8 * (ochk & 3) < kvalid;
     auto store_tile = [&](int q) {
         const int part = q < NQ / 2 ? 0 : 1;
-        bf16* base = (part ? b_cm : a_cm) + ((size_t)bidx * C + (q - part * (NQ / 2)) * 16) * NN + cm0;
+        bf16* base = (part ? b_cm : a_cm) + ((size_t)bidx * C + (q - part * (NQ / 2)) * 16) * slab_ab + spos;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int r = orow + 8 * i;
             const u32x4 v = *reinterpret_cast<const u32x4*>(otile + r * 128 + (((2 * ochk) ^ (2 * (r >> 1))) << 3));
-            bf16* p = (full || 8 * ochk < mvalid) ? base + (size_t)r * NN + 8 * ochk : sink + lane * 8;
+            bf16* p = (full || olive) ? base + (size_t)r * slab_ab : sink + lane * 8;
             *reinterpret_cast<u32x4*>(p) = v;
         }
     };
@@ -576,13 +601,8 @@ static hipError_t launch_k1_fold(const Params& p, const void* z, const void* mas
                                  int incoming, void* a, void* b, hipStream_t s)
 {
     using namespace k1f;
-    int blocks_per_b;
-    if (!incoming) {
-        const size_t NN = (size_t)N * N;
-        blocks_per_b = (int)((NN + NWV * ROWS - 1) / (NWV * ROWS));
-    } else {
-        blocks_per_b = ((N + ROWS - 1) / ROWS) * (N / NWV);
-    }
+    const long long units = (long long)(N / 2) * ((N + 31) / 32);   // 64-pair units per batch element
+    const int blocks_per_b = (int)((units + NWV - 1) / NWV);
     dim3 grid((unsigned)((size_t)B * blocks_per_b));
     hipLaunchKernelGGL((k1_project_fold<D>), grid, dim3(256), 0, s, (const bf16*)z, (const bf16*)mask,
                        (const bf16*)p.w_proj_f, (const bf16*)p.x_proj, p.eps, (bf16*)a, (bf16*)b,

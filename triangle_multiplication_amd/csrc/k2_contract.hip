@@ -4,7 +4,10 @@
 //
 // The projection kernel stores a and b channel-major with k contiguous for both
 // directions (the incoming direction's transpose is folded into that store), so
-// this is always an "NT" product of two K-contiguous operands.
+// this is always an "NT" product of two K-contiguous operands.  fp32 operand
+// slabs are plain [row][k]; bf16 slabs are K-blocked (kblk_off: blocks of 32 k
+// holding all rows), so every K-step of every kernel here reads whole
+// contiguous runs.  o is always plain [i][j].
 //
 // Tiling: a 256-thread workgroup (4 waves in a 2 x 2 grid) owns a BM x BN tile
 // of o; each wave owns (BM/2) x (BN/2) as 16 x 16 MFMA blocks.  K advances 128
@@ -51,9 +54,17 @@ __global__ __launch_bounds__(256) void k2_contract(const T* __restrict__ A, cons
     const int gm = min(GM, tiles_i - first_i);
     const int ti = first_i + (t % (GM * tiles_j)) % gm;
     const int tj = (t % (GM * tiles_j)) / gm;
-    const T* Ab = A + bc * slab;
-    const T* Bb = Bm + bc * slab;
+    constexpr bool KBLK = sizeof(T) == 2;                   // bf16 operands are K-blocked
+    const size_t aslab = ab_slab_elems(KBLK ? DType::BF16 : DType::FP32, N);
+    const T* Ab = A + bc * aslab;
+    const T* Bb = Bm + bc * aslab;
     T* Ob = O + bc * slab;
+    // Element offset of the chunk starting at (row, k); a chunk never crosses
+    // a 32-element block.
+    auto opoff = [&](int row, int k) -> size_t {
+        if constexpr (KBLK) return kblk_off((uint32_t)row, (uint32_t)k, (uint32_t)N);
+        else return (size_t)row * N + k;
+    };
     const int i0 = ti * BM, j0 = tj * BN;
 
     u32x4 ra[A_LD], rb[B_LD];
@@ -64,13 +75,13 @@ __global__ __launch_bounds__(256) void k2_contract(const T* __restrict__ A, cons
         for (int it = 0; it < A_LD; ++it) {
             int q = tid + 256 * it, row = q >> 3, c = q & 7;
             int gi = i0 + row, gk = k0 + c * CE;
-            ra[it] = (gi < N && gk < N) ? ld16(Ab + (size_t)gi * N + gk) : zero;
+            ra[it] = (gi < N && gk < N) ? ld16(Ab + opoff(gi, gk)) : zero;
         }
 #pragma unroll
         for (int it = 0; it < B_LD; ++it) {
             int q = tid + 256 * it, row = q >> 3, c = q & 7;
             int gj = j0 + row, gk = k0 + c * CE;
-            rb[it] = (gj < N && gk < N) ? ld16(Bb + (size_t)gj * N + gk) : zero;
+            rb[it] = (gj < N && gk < N) ? ld16(Bb + opoff(gj, gk)) : zero;
         }
     };
     auto sstore = [&](int buf) {
@@ -140,9 +151,11 @@ __global__ __launch_bounds__(256) void k2_contract(const T* __restrict__ A, cons
 //
 // K advances 32 per step.  The operand rows of a step (64 bytes each, 256 rows
 // of a and 256 of b = 32 KB) live in a ring of LDS slots filled by
-// buffer_load ... lds (global -> LDS without registers); offsets past the end of
-// the slab read as zero, which covers ragged rows and the K tail, and lets the
-// ring run past the last step without tail code.
+// buffer_load ... lds (global -> LDS without registers).  K chunks past N and
+// steps past the workgroup's last tile are pushed out of the buffer's range
+// and read as zero, so the ring runs past the last step without tail code;
+// tile rows past N read zeros or other rows' data, which reach only outputs
+// that are not stored.
 //
 // LDS layout of one operand in one slot (256 rows x 4 chunks of 16 bytes):
 // rows are paired into 128-byte lines, line L = row / 2 holds the 16-byte slot
@@ -168,6 +181,12 @@ __device__ inline int slot_off(int row, int chunk)
 
 #define TRIMUL_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
+// Persistent kernel: one 512-thread workgroup per CU walks its tiles g, g + G,
+// ... in an XCD-banded order (workgroup g runs on XCD g % 8, each XCD gets a
+// compact band of tiles, walked in groups of GM row panels column by column,
+// so the ~32 tiles an XCD runs at once share K-slices of a few panels in its
+// L2; GM = 8 measured best against 1, 2, 4 and 16 at N = 4096).
+//
 // 8 waves in a 2 x 4 grid, each owning a 128 x 64 block of the tile (8 x 4
 // MFMA tiles, 128 accumulators per lane); the two waves that share a SIMD
 // (wave w and w + 4) run half a step apart ("ping-pong").  Each wave
@@ -175,10 +194,10 @@ __device__ inline int slot_off(int row, int chunk)
 // share of step k+3's DMA) and a compute phase C_k (32 MFMAs); group 0 (waves
 // 0-3) is one phase ahead of group 1 (waves 4-7), so in every phase one wave of
 // each SIMD multiplies while the other loads, and phases are separated by one
-// workgroup barrier.
+// workgroup barrier.  Steps are numbered across the workgroup's tiles.
 //
 // Phase p: group 0 runs M_{p/2} (p even) or C_{(p-1)/2} (p odd); group 1 runs
-// the same one phase later.  Invariants (NS = 4 slots, DMA three steps ahead):
+// the same one phase later.  Invariants (NSP = 4 slots, DMA three steps ahead):
 //  - step k's slot is read in phases 2k (group 0) and 2k+1 (group 1); every
 //    wave's DMA share of step k was issued at least four phases earlier, and
 //    before each barrier a wave waits until at most two of its steps are in
@@ -188,131 +207,18 @@ __device__ inline int slot_off(int row, int chunk)
 //    memory phase ends with lgkmcnt(0) so its reads are complete at that barrier.
 // Group 1 takes one extra barrier at the start and group 0 one at the end, so
 // every wave executes the same number of barriers.
-template <int NSP>
-__global__ __launch_bounds__(512) void k2_contract_pp(const bf16* __restrict__ A,
-                                                      const bf16* __restrict__ Bm,
-                                                      bf16* __restrict__ O, int N)
-{
-    using namespace k2big;
-    constexpr int NW = 8;
-    constexpr int DPO = OPB / 1024 / NW;            // DMA instructions per wave per operand (2)
-    constexpr int DPS = 2 * DPO;                    // per wave per step
-    constexpr int DIST = NSP - 1;                   // DMA runs this many steps ahead
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[NSP * STB];
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 2, wn = wave & 3;        // group = wm
-    const size_t slab = (size_t)N * N;
-
-    const int tiles = (N + BM - 1) / BM;
-    const int per_bc = tiles * tiles;
-    const unsigned total = gridDim.x;
-    const unsigned g = blockIdx.x;
-    const unsigned logical = (g & 7u) * (total >> 3) + (g >> 3);
-    const size_t bc = logical / per_bc;
-    const int t = (int)(logical % per_bc);
-    constexpr int GM = 8;   // row panels per group (measured: 8 beats 1, 2, 4 and 16 at N = 4096)
-    const int first_i = (t / (GM * tiles)) * GM;
-    const int gm = min(GM, tiles - first_i);
-    const int ti = first_i + (t % (GM * tiles)) % gm;
-    const int tj = (t % (GM * tiles)) / gm;
-    const int i0 = ti * BM, j0 = tj * BN;
-
-    const unsigned nrec = (unsigned)(slab * sizeof(bf16));
-    __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)(A + bc * slab), 0, nrec, 0x00020000);
-    __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void*)(Bm + bc * slab), 0, nrec, 0x00020000);
-
-    const int dpos = (lane & 7) ^ (lane >> 3);
-    const int dr = 2 * (lane >> 3) + (dpos >> 2), dc = dpos & 3;
-    const unsigned qstride = (unsigned)N * 32u;
-    const unsigned offa0 = (unsigned)(i0 + wave * 16 * DPO + dr) * (unsigned)N * 2u + dc * 16u;
-    const unsigned offb0 = (unsigned)(j0 + wave * 16 * DPO + dr) * (unsigned)N * 2u + dc * 16u;
-    const int nk = (N + BK - 1) / BK;
-
-    auto issue = [&](int step) {
-        unsigned char* st = smem + (step % NSP) * STB + wave * DPO * 1024;
-        const int k0 = step * BK;
-        const unsigned kb = (unsigned)k0 * 2u;
-        const unsigned kpen = (k0 + dc * 8 < N) ? 0u : 0x80000000u;
-#pragma unroll
-        for (int q = 0; q < DPO; ++q) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, TRIMUL_LDS_PTR(st + q * 1024), 16,
-                                                     (offa0 + q * qstride + kb) | kpen, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, TRIMUL_LDS_PTR(st + OPB + q * 1024), 16,
-                                                     (offb0 + q * qstride + kb) | kpen, 0, 0, 0);
-        }
-    };
-
-    const int rchunk = lane >> 4;
-    const int fa_base = slot_off(wm * 128 + (lane & 15), rchunk);
-    const int fb_base = OPB + slot_off(wn * 64 + (lane & 15), rchunk);
-
-    f32x4 acc[8][4];
-#pragma unroll
-    for (int m = 0; m < 8; ++m)
-#pragma unroll
-        for (int n = 0; n < 4; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    u32x4 fa[8], fb[4];
-    // Nothing may be scheduled across a phase boundary (MFMAs included).
-    auto barrier = [&]() {
-        __builtin_amdgcn_sched_barrier(0);
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_sched_barrier(0);
-    };
-
-#pragma unroll
-    for (int s0 = 0; s0 < DIST; ++s0) issue(s0);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm((DIST - 1) * DPS));   // own share of step 0 landed
-    barrier();                                          // ... everyone's
-    if (wm == 1) barrier();                             // group 1 starts one phase late
-
-    for (int step = 0; step < nk; ++step) {
-        // M_step
-        const unsigned char* st = smem + (step % NSP) * STB;
-#pragma unroll
-        for (int m = 0; m < 8; ++m) fa[m] = *reinterpret_cast<const u32x4*>(st + fa_base + m * 1024);
-#pragma unroll
-        for (int n = 0; n < 4; ++n) fb[n] = *reinterpret_cast<const u32x4*>(st + fb_base + n * 1024);
-        issue(step + DIST);
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lds0((DIST - 1) * DPS));
-        barrier();
-        // C_step.  Operands swapped (b rows as the MFMA's A): each lane's four
-        // results are four consecutive j of one i.
-#pragma unroll
-        for (int m = 0; m < 8; ++m)
-#pragma unroll
-            for (int n = 0; n < 4; ++n) acc[m][n] = Elem<bf16>::mma(fb[n], fa[m], acc[m][n]);
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm((DIST - 1) * DPS));
-        barrier();
-    }
-    if (wm == 0) barrier();                             // balance group 1's extra barrier
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));          // no DMA may outlive the workgroup
-
-    bf16* Ob = O + bc * slab;
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-        const int i = i0 + wm * 128 + m * 16 + (lane & 15);
-#pragma unroll
-        for (int n = 0; n < 4; ++n) {
-            const int j = j0 + wn * 64 + n * 16 + 4 * (lane >> 4);
-            if (i < N && j < N) Elem<bf16>::store4(Ob, (size_t)i * N + j, acc[m][n]);
-        }
-    }
-}
-
-// Persistent form of k2_contract_pp: one workgroup per CU walks its tiles
-// g, g + G, ... (the same XCD-banded tile order), and the step sequence runs
-// on across tile boundaries -- the DMA ring is never drained, so the next
-// tile's first steps are in flight while the current one finishes, and a
-// tile's stores overlap the next tile's multiplies.  Each workgroup starts its
-// K loop at its own offset (the sum's order does not matter), which spreads
-// the tile boundaries, and so the store bursts, over time.  A wave stores its
-// block and clears its accumulators right after the compute phase of a
-// tile's last step; both groups do this at the same point of their own phase
-// sequence, so every wave still executes the same barriers.
+//
+// The DMA ring is never drained between tiles: the next tile's first steps
+// are in flight while the current one finishes, and a tile's stores overlap
+// the next tile's multiplies.  A wave stores its block and clears its
+// accumulators right after the compute phase of a tile's last step; both
+// groups do this at the same point of their own phase sequence, so every wave
+// still executes the same barriers.
+//
+// Operands are K-blocked (kblk_off): a step's 256 rows of one operand are one
+// contiguous 16 KB run, and each DMA instruction reads one contiguous
+// kilobyte (16 rows x 64 bytes).  With row-major operands the same step reads
+// 256 half cache lines 2N bytes apart, which measured 12 % slower overall.
 template <int NSP>
 __global__ __launch_bounds__(512) void k2_contract_ppp(const bf16* __restrict__ A,
                                                        const bf16* __restrict__ Bm,
@@ -334,11 +240,11 @@ __global__ __launch_bounds__(512) void k2_contract_ppp(const bf16* __restrict__ 
     const int G = gridDim.x, g = blockIdx.x;
     const int n_my = (total - g + G - 1) / G;       // tiles of this workgroup (g < total)
     const int nk = (N + BK - 1) / BK;
-    const int koff = 0;   // rotating the K loop per workgroup loses the L2 sharing of K-slices
     const int S = n_my * nk;                        // steps of this workgroup (< 2^31)
 
     // Tile tl of this workgroup: virtual block g + tl*G through the XCD-banded
-    // order (total and G are multiples of 8, so the band is g's).
+    // order, a bijection of [0, total) because total is a multiple of 8 (C is);
+    // with G a multiple of 8 every tile of workgroup g lies in g's band.
     auto tile_geo = [&](int tl, size_t& bc, int& i0, int& j0) {
         const unsigned vb = (unsigned)g + (unsigned)tl * (unsigned)G;
         const unsigned logical = (vb & 7u) * ((unsigned)total >> 3) + (vb >> 3);
@@ -351,17 +257,23 @@ __global__ __launch_bounds__(512) void k2_contract_ppp(const bf16* __restrict__ 
         j0 = ((t % (GM * tiles)) / gm) * BN;
     };
 
-    const unsigned nrec = (unsigned)(slab * sizeof(bf16));
+    // Operand slab: [nk][N][32] bf16.  DMA instruction q of a wave covers rows
+    // 16 (DPO wave + q) .. +15 of the tile, one contiguous kilobyte of the
+    // step's block; lane l reads row dr, chunk dc (the slot swizzle is
+    // applied by choosing which lane reads which chunk).
+    const size_t aslab = ab_slab_elems(DType::BF16, N);
+    const unsigned nrec = (unsigned)(aslab * sizeof(bf16));
     const int dpos = (lane & 7) ^ (lane >> 3);
     const int dr = 2 * (lane >> 3) + (dpos >> 2), dc = dpos & 3;
-    const unsigned qstride = (unsigned)N * 32u;
-    const unsigned lane_off = (unsigned)(wave * 16 * DPO + dr) * (unsigned)N * 2u + dc * 16u;
+    constexpr unsigned qstride = 16u * ROWB;
+    const unsigned kstride = (unsigned)N * ROWB;    // bytes per K-block
+    const unsigned lane_off = (unsigned)(wave * 16 * DPO + dr) * ROWB + dc * 16u;
 
     // DMA cursor: the next step to load is K-step ikk of tile itl.  The tile's
     // buffer descriptors and row offsets are recomputed only when the cursor
     // enters a new tile; past the workgroup's last tile (and for K-chunks past
     // N) the offset is pushed beyond the buffer's range, so the DMA reads zeros.
-    int itl = 0, ikk = koff;
+    int itl = 0, ikk = 0;
     __amdgpu_buffer_rsrc_t ra, rb;
     unsigned oa_t = 0, ob_t = 0;
     bool ilive = true;
@@ -369,17 +281,17 @@ __global__ __launch_bounds__(512) void k2_contract_ppp(const bf16* __restrict__ 
         ilive = itl < n_my;
         size_t bc; int i0, j0;
         tile_geo(ilive ? itl : 0, bc, i0, j0);
-        ra = __builtin_amdgcn_make_buffer_rsrc((void*)(A + bc * slab), 0, nrec, 0x00020000);
-        rb = __builtin_amdgcn_make_buffer_rsrc((void*)(Bm + bc * slab), 0, nrec, 0x00020000);
-        oa_t = lane_off + (unsigned)i0 * (unsigned)N * 2u;
-        ob_t = lane_off + (unsigned)j0 * (unsigned)N * 2u;
+        ra = __builtin_amdgcn_make_buffer_rsrc((void*)(A + bc * aslab), 0, nrec, 0x00020000);
+        rb = __builtin_amdgcn_make_buffer_rsrc((void*)(Bm + bc * aslab), 0, nrec, 0x00020000);
+        oa_t = lane_off + (unsigned)i0 * ROWB;
+        ob_t = lane_off + (unsigned)j0 * ROWB;
     };
     set_tile();
     int isl = 0;                                    // ring slot of the next step
     auto issue = [&]() {
         unsigned char* st = smem + isl * STB + wave * DPO * 1024;
         const int k0 = ikk * BK;
-        const unsigned kb = (unsigned)k0 * 2u;
+        const unsigned kb = (unsigned)ikk * kstride;
         const unsigned kpen = (ilive && k0 + dc * 8 < N) ? 0u : 0x80000000u;
 #pragma unroll
         for (int q = 0; q < DPO; ++q) {
@@ -389,8 +301,7 @@ __global__ __launch_bounds__(512) void k2_contract_ppp(const bf16* __restrict__ 
                                                      (ob_t + q * qstride + kb) | kpen, 0, 0, 0);
         }
         if (++isl == NSP) isl = 0;
-        if (++ikk == nk) ikk = 0;
-        if (ikk == koff) { ++itl; set_tile(); }
+        if (++ikk == nk) { ikk = 0; ++itl; set_tile(); }
     };
 
     const int rchunk = lane >> 4;
@@ -481,11 +392,6 @@ hipError_t launch_contract(const Params& p, const void* a_cm, const void* b_cm, 
     const bool big = N >= 1024 && (N % 256 == 0 || N >= 2048);
     if (p.dtype == DType::BF16 && big) {
         const int tiles = (N + k2big::BM - 1) / k2big::BM;
-        dim3 grid((unsigned)((size_t)tiles * tiles * B * p.C));
-#ifdef TRIMUL_K2_NONPERSISTENT
-        hipLaunchKernelGGL(k2_contract_pp<4>, grid, dim3(512), 0, s, (const bf16*)a_cm,
-                           (const bf16*)b_cm, (bf16*)o, N);
-#else
         const long long total = (long long)tiles * tiles * B * p.C;
         int dev = 0, cus = 256;
         if (hipGetDevice(&dev) == hipSuccess)
@@ -493,7 +399,6 @@ hipError_t launch_contract(const Params& p, const void* a_cm, const void* b_cm, 
         const long long pg = total < cus ? total : cus;
         hipLaunchKernelGGL(k2_contract_ppp<4>, dim3((unsigned)pg), dim3(512), 0, s, (const bf16*)a_cm,
                            (const bf16*)b_cm, (bf16*)o, N, (int)total);
-#endif
         return hipGetLastError();
     }
     if (p.dtype == DType::BF16) return launch_k2<bf16, 128, 128>(a_cm, b_cm, B, p.C, N, o, s);

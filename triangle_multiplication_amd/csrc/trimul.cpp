@@ -177,8 +177,10 @@ trimul_status trimul_workspace_query(int D, int C, trimul_dtype dtype, int B, in
     if (!width_ok(D) || !width_ok(C))
         return fail(TRIMUL_ERR_UNSUPPORTED, "D and C must be multiples of 32 in [32, 256]; got D=%d C=%d", D, C);
     if (B < 1 || N < 1) return fail(TRIMUL_ERR_INVALID_ARG, "B and N must be >= 1; got B=%d N=%d", B, N);
-    const size_t slab = align256((size_t)B * C * (size_t)N * N * elem_size(dtype));
-    *bytes = 3 * slab;
+    const trimul::DType t = dtype == TRIMUL_BF16 ? trimul::DType::BF16 : trimul::DType::FP32;
+    const size_t ab = align256((size_t)B * C * trimul::ab_slab_elems(t, N) * elem_size(dtype));
+    const size_t o = align256((size_t)B * C * (size_t)N * N * elem_size(dtype));
+    *bytes = 2 * ab + o;
     return ok();
 }
 
@@ -355,11 +357,11 @@ trimul_status trimul_fwd(trimul_handle* h, const void* z, const void* pair_mask,
     st = check_handle_device(h);
     if (st != TRIMUL_OK) return st;
 
-    const size_t slab = align256((size_t)B * h->p.C * NN * es);
+    const size_t ab = align256((size_t)B * h->p.C * trimul::ab_slab_elems(h->p.dtype, N) * es);
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     void* a = ws;
-    void* b = ws + slab;
-    void* o = ws + 2 * slab;
+    void* b = ws + ab;
+    void* o = ws + 2 * ab;
     hipError_t e = trimul::launch_project(h->p, z, pair_mask, B, N, dir == TRIMUL_INCOMING, a, b, stream);
     if (e != hipSuccess) return hip_fail("projection kernel launch", e);
     e = trimul::launch_contract(h->p, a, b, B, N, o, stream);

@@ -97,6 +97,17 @@ __device__ inline float sum_row_lanes(float v) {
     return v;
 }
 
+// bf16 storage of the gated projections a and b is K-blocked: a slab of N
+// rows is cut into blocks of 32 consecutive k, and a block holds all N rows
+// of those 32 k (64 bytes per row), i.e. [ceil(N/32)][N][32].  A K-step of the
+// contraction then reads one contiguous 64-byte run per row, and 16 rows in
+// one contiguous kilobyte.  Element offset of (row, k); below 2^31 for every
+// N the library accepts.
+__device__ inline uint32_t kblk_off(uint32_t row, uint32_t k, uint32_t N)
+{
+    return ((k >> 5) * N + row) * 32u + (k & 31u);
+}
+
 // LDS swizzle for row-major tiles of 16-byte chunks: the low three bits of the
 // chunk index are XORed with the row, so eight consecutive rows reading the same
 // logical chunk hit eight distinct 128-byte bank groups.

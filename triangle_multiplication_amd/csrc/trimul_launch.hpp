@@ -41,6 +41,15 @@ struct Params {
     void* sink;
 };
 
+// Elements of one (batch, channel) slab of a and b in the workspace.  bf16:
+// K-blocked [Kp/32][N][32] with Kp = N rounded up to a multiple of 32 (k >= N
+// is padding that no kernel reads); fp32: plain row-major [N][N].
+__host__ __device__ inline size_t ab_slab_elems(DType t, int N)
+{
+    const size_t n = (size_t)N;
+    return t == DType::BF16 ? n * ((n + 31) & ~(size_t)31) : n * n;
+}
+
 hipError_t launch_project(const Params& p, const void* z, const void* mask, int B, int N,
                           int incoming, void* a_cm, void* b_cm, hipStream_t s);
 hipError_t launch_contract(const Params& p, const void* a_cm, const void* b_cm, int B, int N,
