@@ -509,9 +509,13 @@ __global__ __launch_bounds__(256, 2) void k1_project_fold(
                 for (int k = lo; k < hi; ++k) epi_out(hpc, k, pp, gp, ov);
             }
             // Alternate MFMAs with the epilogue arithmetic inside the step.
-            __builtin_amdgcn_sched_group_barrier(0x0100, 4, 0);            // LDS reads
+            // The next step's LDS reads go after this step's first MFMA: the
+            // compiler waits for every outstanding LDS read before an MFMA, so
+            // reads issued ahead of it would be waited for at once.
 #pragma unroll
             for (int m = 0; m < 2 * HB; ++m) {
+                if (m == 1)
+                    __builtin_amdgcn_sched_group_barrier(0x0100, 4, 0);    // LDS reads
                 __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);        // MFMA
                 __builtin_amdgcn_sched_group_barrier(0x0402, 3, 0);        // VALU / transcendental
             }

@@ -18,6 +18,7 @@
 #include "trimul_device.hpp"
 #include "trimul_launch.hpp"
 
+
 namespace trimul {
 
 template <typename T, int D, int C>
@@ -259,6 +260,46 @@ struct Cfg {
 };
 }  // namespace k3f
 
+// The o operand of one 16-pair block, KG fragments of 16 bytes, each made of two
+// transposing 8-byte LDS reads at base + 2048 kg and base + 2048 kg + 256.  One
+// asm block issues all of them and waits for them: the compiler places a wait
+// for every outstanding global->LDS DMA before each transposing-read builtin
+// (it cannot tell that the read does not touch the slots in flight), which
+// would drain the prefetch ring on every tile.  The slots read here have
+// landed by the kernel's own vmcnt waits and barriers.
+template <int KG> struct OFrags;
+#define TRIMUL_TR2(i, off) "ds_read_b64_tr_b16 %" #i ", %[a] offset:" #off "\n\t"
+template <> struct OFrags<8> {
+    __device__ static inline void read(uint32_t a, u32x4 (&y)[8]) {
+        u32x2 r[16];
+        asm volatile(TRIMUL_TR2(0, 0) TRIMUL_TR2(1, 256) TRIMUL_TR2(2, 2048) TRIMUL_TR2(3, 2304)
+                     TRIMUL_TR2(4, 4096) TRIMUL_TR2(5, 4352) TRIMUL_TR2(6, 6144) TRIMUL_TR2(7, 6400)
+                     TRIMUL_TR2(8, 8192) TRIMUL_TR2(9, 8448) TRIMUL_TR2(10, 10240) TRIMUL_TR2(11, 10496)
+                     TRIMUL_TR2(12, 12288) TRIMUL_TR2(13, 12544) TRIMUL_TR2(14, 14336) TRIMUL_TR2(15, 14592)
+                     "s_waitcnt lgkmcnt(0)"
+                     : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
+                       "=&v"(r[6]), "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]),
+                       "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]), "=&v"(r[15])
+                     : [a] "v"(a));
+#pragma unroll
+        for (int k = 0; k < 8; ++k) y[k] = u32x4{r[2 * k][0], r[2 * k][1], r[2 * k + 1][0], r[2 * k + 1][1]};
+    }
+};
+template <> struct OFrags<4> {
+    __device__ static inline void read(uint32_t a, u32x4 (&y)[4]) {
+        u32x2 r[8];
+        asm volatile(TRIMUL_TR2(0, 0) TRIMUL_TR2(1, 256) TRIMUL_TR2(2, 2048) TRIMUL_TR2(3, 2304)
+                     TRIMUL_TR2(4, 4096) TRIMUL_TR2(5, 4352) TRIMUL_TR2(6, 6144) TRIMUL_TR2(7, 6400)
+                     "s_waitcnt lgkmcnt(0)"
+                     : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
+                       "=&v"(r[6]), "=&v"(r[7])
+                     : [a] "v"(a));
+#pragma unroll
+        for (int k = 0; k < 4; ++k) y[k] = u32x4{r[2 * k][0], r[2 * k][1], r[2 * k + 1][0], r[2 * k + 1][1]};
+    }
+};
+#undef TRIMUL_TR2
+
 #define TRIMUL_LDS3(p) ((__attribute__((address_space(3))) void*)(p))
 
 template <int D, int C>
@@ -271,7 +312,6 @@ __global__ __launch_bounds__(512) void k3_output_fold(
     using Cf = Cfg<D, C>;
     constexpr int KGD = Cf::KGD, KGC = Cf::KGC, RBW = Cf::RBW;
     constexpr int ZB = Cf::ZB, SLOT = Cf::SLOT, FRAG = Cf::FRAG, STAT = Cf::STAT;
-    typedef short i16x4 __attribute__((ext_vector_type(4)));
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     __shared__ __attribute__((aligned(1024))) unsigned char smem[Cf::LDS];
     unsigned char* ring = smem;
@@ -355,12 +395,10 @@ __global__ __launch_bounds__(512) void k3_output_fold(
     auto zfrag = [&](const unsigned char* sl, int bb, int kg) -> u32x4 {
         return *reinterpret_cast<const u32x4*>(sl + zb[kg & 3] + 256 * (kg >> 2) + 32 * D * bb);
     };
-    auto ofrag = [&](const unsigned char* sl, int bb, int kg) -> u32x4 {
-        const unsigned char* p = sl + ZB + obb[bb] + 2048 * kg;
-        const i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
-        const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p + 256));
-        const u32x2 h0 = __builtin_bit_cast(u32x2, r0), h1 = __builtin_bit_cast(u32x2, r1);
-        return u32x4{h0[0], h0[1], h1[0], h1[1]};
+    // All KGC o fragments of block bb (OFrags: one asm block, waited for).
+    auto ofrags = [&](const unsigned char* sl, int bb, u32x4 (&yf)[KGC]) {
+        const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)(sl + ZB + obb[bb]);
+        OFrags<KGC>::read(a, yf);
     };
 
     // Statistics of one 16-pair block of tile it (waves 0..3: kind = wave / 2
@@ -386,8 +424,10 @@ __global__ __launch_bounds__(512) void k3_output_fold(
 #pragma unroll
             for (int kg = 0; kg < KGD; ++kg) acc(zfrag(sl, bb, kg));
         } else {
+            u32x4 yf[KGC];
+            ofrags(sl, bb, yf);
 #pragma unroll
-            for (int kg = 0; kg < KGC; ++kg) acc(ofrag(sl, bb, kg));
+            for (int kg = 0; kg < KGC; ++kg) acc(yf[kg]);
         }
         s1 = sum_row_lanes(s1);
         s2 = sum_row_lanes(s2);
@@ -415,6 +455,8 @@ __global__ __launch_bounds__(512) void k3_output_fold(
 #pragma unroll
         for (int bb = 0; bb < NB; ++bb) {
             f32x4 ag[RBW], ay[RBW];
+            u32x4 yfs[KGC];
+            ofrags(sl, bb, yfs);
             const u32x4 xe = *reinterpret_cast<const u32x4*>(st + bb * FRAG + lane * 16);
             const u32x4 ye = *reinterpret_cast<const u32x4*>(st + (NB + bb) * FRAG + lane * 16);
 #pragma unroll
@@ -431,7 +473,7 @@ __global__ __launch_bounds__(512) void k3_output_fold(
             }
 #pragma unroll
             for (int kg = 0; kg < KGC; ++kg) {
-                const u32x4 yf = ofrag(sl, bb, kg);
+                const u32x4 yf = yfs[kg];
 #pragma unroll
                 for (int r = 0; r < RBW; ++r) ay[r] = Elem<bf16>::mma(wp[r][kg], yf, ay[r]);
             }
