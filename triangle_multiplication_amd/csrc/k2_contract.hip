@@ -268,6 +268,14 @@ __global__ __launch_bounds__(512) void k2_contract_ppp(const bf16* __restrict__ 
     constexpr unsigned qstride = 16u * ROWB;
     const unsigned kstride = (unsigned)N * ROWB;    // bytes per K-block
     const unsigned lane_off = (unsigned)(wave * 16 * DPO + dr) * ROWB + dc * 16u;
+    // B rows are loaded permuted within each 32-row group: slot row 16 h + r
+    // (h = 0, 1; r = 0..15) holds tile row 8 (r / 4) + 4 h + r % 4.  After the
+    // MFMAs of blocks 2p and 2p + 1, lane group g then holds the results for
+    // rows 32 p + 8 g .. + 7 of its wave's 64, eight consecutive j of one i,
+    // stored as one 16-byte run.  Instruction q of a wave fills slot rows
+    // 16 (2 wave + q) .. + 15, i.e. h = q and group wave.
+    static_assert(DPO == 2, "B row permutation assumes two DMA instructions per operand per wave");
+    const unsigned lane_off_b = (unsigned)(32 * wave + 8 * (dr >> 2) + (dr & 3)) * ROWB + dc * 16u;
 
     // DMA cursor: the next step to load is K-step ikk of tile itl.  The tile's
     // buffer descriptors and row offsets are recomputed only when the cursor
@@ -284,7 +292,7 @@ __global__ __launch_bounds__(512) void k2_contract_ppp(const bf16* __restrict__ 
         ra = __builtin_amdgcn_make_buffer_rsrc((void*)(A + bc * aslab), 0, nrec, 0x00020000);
         rb = __builtin_amdgcn_make_buffer_rsrc((void*)(Bm + bc * aslab), 0, nrec, 0x00020000);
         oa_t = lane_off + (unsigned)i0 * ROWB;
-        ob_t = lane_off + (unsigned)j0 * ROWB;
+        ob_t = lane_off_b + (unsigned)j0 * ROWB;
     };
     set_tile();
     int isl = 0;                                    // ring slot of the next step
@@ -298,7 +306,7 @@ __global__ __launch_bounds__(512) void k2_contract_ppp(const bf16* __restrict__ 
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, TRIMUL_LDS_PTR(st + q * 1024), 16,
                                                      (oa_t + q * qstride + kb) | kpen, 0, 0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, TRIMUL_LDS_PTR(st + OPB + q * 1024), 16,
-                                                     (ob_t + q * qstride + kb) | kpen, 0, 0, 0);
+                                                     (ob_t + q * 4u * ROWB + kb) | kpen, 0, 0, 0);
         }
         if (++isl == NSP) isl = 0;
         if (++ikk == nk) { ikk = 0; ++itl; set_tile(); }
@@ -360,10 +368,18 @@ __global__ __launch_bounds__(512) void k2_contract_ppp(const bf16* __restrict__ 
             for (int m = 0; m < 8; ++m) {
                 const int i = i0 + wm * 128 + m * 16 + (lane & 15);
 #pragma unroll
-                for (int n = 0; n < 4; ++n) {
-                    const int j = j0 + wn * 64 + n * 16 + 4 * (lane >> 4);
-                    if (i < N && j < N) Elem<bf16>::store4(Ob, (size_t)i * N + j, acc[m][n]);
-                    acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int p = 0; p < 2; ++p) {
+                    // j .. j + 7 (8 divides N, so all or none exist)
+                    const int j = j0 + wn * 64 + 32 * p + 8 * (lane >> 4);
+                    bf16x8 h;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        h[e] = (bf16)acc[m][2 * p][e];
+                        h[4 + e] = (bf16)acc[m][2 * p + 1][e];
+                    }
+                    if (i < N && j < N) *reinterpret_cast<bf16x8*>(Ob + (size_t)i * N + j) = h;
+                    acc[m][2 * p] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    acc[m][2 * p + 1] = f32x4{0.f, 0.f, 0.f, 0.f};
                 }
             }
             kin = 0;
