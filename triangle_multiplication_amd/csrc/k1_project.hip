@@ -313,9 +313,8 @@ __global__ __launch_bounds__(256, 2) void k1_project_fold(
         const int row = byte / (2 * D), pch = (byte % (2 * D)) / 16;
         doff[i] = (uint32_t)(row * D + (pch ^ (row & 15)) * 8);
     }
-    auto issue = [&](int q) {
+    auto issue = [&](int q, unsigned char* sl) {
         const bf16* w0 = Wf + (size_t)q * 32 * D;
-        unsigned char* sl = ring + (q % NSW) * STAGE;
 #pragma unroll
         for (int i = 0; i < DPW; ++i)
             __builtin_amdgcn_global_load_lds(
@@ -330,9 +329,9 @@ __global__ __launch_bounds__(256, 2) void k1_project_fold(
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    issue(0);
-    issue(1);
-    issue(2);   // NQ = C / 8 >= 4
+    issue(0, ring);
+    issue(1, ring + STAGE);
+    issue(2, ring + 2 * STAGE);   // NQ = C / 8 >= 4
     for (int i = tid; i < 4 * C; i += 256) ext[i] = ld16(Xf + (size_t)i * 8);
     if (wave == 0)
 #pragma unroll
@@ -531,11 +530,18 @@ __global__ __launch_bounds__(256, 2) void k1_project_fold(
     Pre cur;
     load_corr(I0{}, 0, cur);
     half(I0{}, F_{}, I1{}, I1{}, ring, 0, cur, pA, gA, 0, pB, gB, 0);
-    for (int q = 0;; ++q) {
-        const unsigned char* sl = ring + (q % NSW) * STAGE;
+    // One iteration of the stage loop: the second half of stage q (ring slot
+    // S = q % NSW) and the first half of stage q + 1.  S is a constant in each
+    // of the NSW unrolled copies, so every LDS address of an iteration is a
+    // loop-invariant register plus an immediate offset.  Returns true after
+    // the last stage's second half has been issued.
+    static_assert(NSW == 3, "the stage loop is unrolled by the ring depth");
+    auto iteration = [&](auto sc, int q) -> bool {
+        constexpr int S = decltype(sc)::value;
+        const unsigned char* sl = ring + S * STAGE;
         const int qn = q + 1 < NQ ? q + 1 : q;
         half(I1{}, T_{}, I0{}, I0{}, sl, q, cur, pB, gB, q, pA, gA, qn);
-        if (q + 1 == NQ) break;
+        if (q + 1 == NQ) return true;
         // Stage q + 1 must have landed.  Every wave issues, in this order per
         // iteration: the DMA of stage q + 3 (DPW instructions, while q + 3 <
         // NQ) and the two stores of stage q.  Stage q + 1's DMA was issued in
@@ -547,9 +553,15 @@ __global__ __launch_bounds__(256, 2) void k1_project_fold(
         else if (q + 2 < NQ) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lds0(DPW + 2));
         else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lds0(2));
         barrier();
-        if (q + 3 < NQ) issue(q + 3);    // into the slot stage q used
-        half(I0{}, T_{}, I1{}, I1{}, ring + ((q + 1) % NSW) * STAGE, q + 1, cur, pA, gA, q, pB, gB, q + 1);
+        if (q + 3 < NQ) issue(q + 3, ring + S * STAGE);   // into the slot stage q used
+        half(I0{}, T_{}, I1{}, I1{}, ring + ((S + 1) % NSW) * STAGE, q + 1, cur, pA, gA, q, pB, gB, q + 1);
         store_tile(q);                   // the tile is complete; stage q + 1's epilogue starts after
+        return false;
+    };
+    for (int q = 0;; q += NSW) {
+        if (iteration(std::integral_constant<int, 0>{}, q)) break;
+        if (iteration(std::integral_constant<int, 1>{}, q + 1)) break;
+        if (iteration(std::integral_constant<int, 2>{}, q + 2)) break;
     }
     {
         f32x4 ov[HB];
