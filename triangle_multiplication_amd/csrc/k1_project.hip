@@ -249,8 +249,6 @@ struct Cfg {
 };
 }  // namespace k1f
 
-#define TRIMUL_K1_LDS3(p) ((__attribute__((address_space(3))) void*)(p))
-
 template <int D>
 __global__ __launch_bounds__(256, 2) void k1_project_fold(
     const bf16* __restrict__ z, const bf16* __restrict__ mask, const bf16* __restrict__ Wf,
@@ -313,13 +311,14 @@ __global__ __launch_bounds__(256, 2) void k1_project_fold(
         const int row = byte / (2 * D), pch = (byte % (2 * D)) / 16;
         doff[i] = (uint32_t)(row * D + (pch ^ (row & 15)) * 8);
     }
-    auto issue = [&](int q, unsigned char* sl) {
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+    const uint32_t lds_ring = lds_addr_of(ring);
+    auto issue = [&](int q, const unsigned char* sl) {
         const bf16* w0 = Wf + (size_t)q * 32 * D;
+        const uint32_t la = lds_ring + (uint32_t)(sl - ring) + (uint32_t)(wave_s * 1024);
 #pragma unroll
         for (int i = 0; i < DPW; ++i)
-            __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void*)(w0 + (i >> 1) * 16 * D + doff[i & 1]),
-                TRIMUL_K1_LDS3(sl + (wave + i * NWV) * 1024), 16, 0, 0);
+            dma16_to_lds(w0 + (i >> 1) * 16 * D + doff[i & 1], la + (uint32_t)(i * NWV * 1024));
     };
     auto barrier = [&]() {
         __builtin_amdgcn_sched_barrier(0);
@@ -508,9 +507,8 @@ __global__ __launch_bounds__(256, 2) void k1_project_fold(
                 for (int k = lo; k < hi; ++k) epi_out(hpc, k, pp, gp, ov);
             }
             // Alternate MFMAs with the epilogue arithmetic inside the step.
-            // The next step's LDS reads go after this step's first MFMA: the
-            // compiler waits for every outstanding LDS read before an MFMA, so
-            // reads issued ahead of it would be waited for at once.
+            // The next step's LDS reads go after this step's first MFMA
+            // (measured against before it and after the second or third).
 #pragma unroll
             for (int m = 0; m < 2 * HB; ++m) {
                 if (m == 1)

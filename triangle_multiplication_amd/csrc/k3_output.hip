@@ -300,7 +300,6 @@ template <> struct OFrags<4> {
 };
 #undef TRIMUL_TR2
 
-#define TRIMUL_LDS3(p) ((__attribute__((address_space(3))) void*)(p))
 
 template <int D, int C>
 __global__ __launch_bounds__(512) void k3_output_fold(
@@ -348,28 +347,28 @@ __global__ __launch_bounds__(512) void k3_output_fold(
     // DMA of tile it into ring slot it % NS.  Instruction q covers 1 KB of the
     // slot; lane l fills its 16 bytes.  Phantom tiles (past the end) re-read
     // tile 0 so that every wave issues the same count.
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+    const uint32_t lds_ring = lds_addr_of(ring);
     auto issue = [&](int it) {
         const size_t p0 = tile_p0(it);
         const size_t bidx = p0 / NN, pin = p0 % NN;
-        unsigned char* sl = ring + (it & (NS - 1)) * SLOT;
+        const uint32_t sl = lds_ring + (uint32_t)((it & (NS - 1)) * SLOT);
         int ln = threadIdx.x & 63;      // opaque: keeps per-lane offsets out of loop-carried registers
         asm volatile("" : "+v"(ln));
 #pragma unroll
         for (int i = 0; i < Cf::DPW; ++i) {
-            const int q = wave + i * NW;
+            const int q = wave_s + i * NW;
             if (q < Cf::ZDMA) {
                 const int byte = q * 1024 + ln * 16;
                 const int row = byte / (D * 2), pch = (byte % (D * 2)) / 16;
                 const bf16* src = z + (p0 + row) * D + (pch ^ (row & 15)) * 8;
-                __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                                 TRIMUL_LDS3(sl + q * 1024), 16, 0, 0);
+                dma16_to_lds(src, sl + (uint32_t)(q * 1024));
             } else {
                 const int qo = q - Cf::ZDMA;
                 const int c = qo * 16 + (ln >> 2), pc = ln & 3;
                 const int half = (pc >> 1) ^ ((c >> 3) & 1);
                 const bf16* src = o + (bidx * C + c) * NN + pin + half * 16 + (pc & 1) * 8;
-                __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                                 TRIMUL_LDS3(sl + ZB + qo * 1024), 16, 0, 0);
+                dma16_to_lds(src, sl + (uint32_t)(ZB + qo * 1024));
             }
         }
     };
@@ -397,7 +396,7 @@ __global__ __launch_bounds__(512) void k3_output_fold(
     };
     // All KGC o fragments of block bb (OFrags: one asm block, waited for).
     auto ofrags = [&](const unsigned char* sl, int bb, u32x4 (&yf)[KGC]) {
-        const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)(sl + ZB + obb[bb]);
+        const uint32_t a = lds_addr_of(sl + ZB + obb[bb]);
         OFrags<KGC>::read(a, yf);
     };
 

@@ -117,6 +117,24 @@ __device__ inline int swz(int row, int chunk) { return chunk ^ (row & 7); }
 // swizzled index inside the row (n is a multiple of 4 for all widths used).
 constexpr int swz_mask(int n) { return n % 8 == 0 ? 7 : n % 4 == 0 ? 3 : n % 2 == 0 ? 1 : 0; }
 
+// Global -> LDS DMA of 16 bytes per lane: lane l's 16 bytes at gaddr land at
+// LDS byte lds_addr + 16 l (lds_addr wave-uniform; it goes through M0).
+// Issued as inline asm rather than through the builtin: after the builtin the
+// compiler cannot tell which LDS reads a pending DMA may feed, and answers
+// every later LDS read wait with a full lgkmcnt(0) (or, before a transposing
+// read, vmcnt(0)).  Completion is the caller's business: each kernel waits
+// on vmcnt explicitly before a barrier that publishes the slot.
+__device__ inline void dma16_to_lds(const void* gaddr, uint32_t lds_addr)
+{
+    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gaddr), "{m0}"(lds_addr) : "memory");
+}
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ inline uint32_t lds_addr_of(const void* p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
 // s_waitcnt immediate for "vmcnt <= n" leaving expcnt and lgkmcnt unconstrained
 // (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
 constexpr int waitcnt_vm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4) | (15 << 8); }
