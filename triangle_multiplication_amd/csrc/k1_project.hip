@@ -290,8 +290,12 @@ __global__ __launch_bounds__(256, 2) void k1_project_fold(
     //   incoming: storage row i = z column, k = z row: z pair (k, row)
     const int nkb = (N + 31) / 32;
     const int unit = t * NWV + wave;
-    const int row0 = 2 * (unit / nkb), k0 = 32 * (unit % nkb);
-    const int kvalid = row0 < N ? min(32, N - k0) : 0;   // the last workgroup may hold idle waves
+    // Consecutive units take consecutive row pairs of one k block, so the
+    // lines the workgroups in flight store are one contiguous run per channel
+    // (measured 1-7 % faster than walking the k blocks of a row pair first).
+    const int npr = N / 2;
+    const int row0 = 2 * (unit % npr), k0 = 32 * (unit / npr);
+    const int kvalid = unit < npr * nkb ? min(32, N - k0) : 0;   // the last workgroup may hold idle waves
     auto zpair = [&](int m) -> size_t {
         const size_t row = (size_t)(row0 + (m >> 5)), k = (size_t)(k0 + (m & 31));
         return incoming ? k * N + row : row * N + k;
