@@ -115,7 +115,11 @@ def test_contract_exact_integers_full_size(tb, C, N):
 # ----------------------------------------------------------------------------
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("direction", ["outgoing", "incoming"])
-@pytest.mark.parametrize("B,N,D,C", [(2, 40, 64, 64), (1, 72, 128, 32), (1, 16, 96, 160)])
+# The bf16 kernel for D in {128, 256} runs C / 8 weight stages through a
+# three-slot ring in a loop unrolled by three: C = 32, 96, 224 give stage
+# counts of every residue mod 3; N = 40, 72 leave a ragged k block.
+@pytest.mark.parametrize("B,N,D,C", [(2, 40, 64, 64), (1, 72, 128, 32), (1, 16, 96, 160),
+                                     (1, 40, 128, 96), (2, 24, 256, 224)])
 def test_project_stage(tb, dtype, direction, B, N, D, C):
     say("project stage", dtype, direction, B, N, D, C)
     w = inputs.make_weights(D, C, dtype, random_ln=True)
@@ -169,7 +173,8 @@ def test_output_stage(tb, dtype, B, N, D, C):
 @pytest.mark.parametrize("direction", ["outgoing", "incoming"])
 @pytest.mark.parametrize("B,N,D,C,masked", [(1, 8, 32, 32, False), (3, 24, 64, 96, True),
                                             (1, 72, 128, 128, True), (2, 136, 32, 64, False),
-                                            (1, 40, 256, 256, True), (1, 48, 160, 32, True)])
+                                            (1, 40, 256, 256, True), (1, 48, 160, 32, True),
+                                            (1, 24, 256, 192, True)])
 def test_fwd_small_shapes(tb, dtype, direction, B, N, D, C, masked):
     say("fwd small", dtype, direction, B, N, D, C, masked)
     w = inputs.make_weights(D, C, dtype, random_ln=True)
