@@ -332,17 +332,11 @@ __global__ __launch_bounds__(256, 2) void k1_project_fold(
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    issue(0, ring);
-    issue(1, ring + STAGE);
-    issue(2, ring + 2 * STAGE);   // NQ = C / 8 >= 4
-    for (int i = tid; i < 4 * C; i += 256) ext[i] = ld16(Xf + (size_t)i * 8);
-    if (wave == 0)
-#pragma unroll
-        for (int i = 0; i < RB * 16 * 16 / (64 * 16); ++i)
-            *reinterpret_cast<u32x4*>(xfa + NWV * RB * 256 + (i * 64 + lane) * 16) = u32x4{0u, 0u, 0u, 0u};
-
-    // Raw z rows as the MFMA A operand: block rb, K-group kg -> chunk kg*4 + g4
-    // of pair rb*16 + l16.  K-group KG is the correction fragment.
+    // Prologue loads, all in flight together: the raw z rows (MFMA A operand:
+    // block rb, K-group kg -> chunk kg*4 + g4 of pair rb*16 + l16) and the mask
+    // into registers, then the correction rows and the first three weight
+    // stages into LDS by DMA.  Lanes of pairs that do not exist read pair 0
+    // and are zeroed afterwards, so no load sits behind a branch.
     u32x4 zf[RB][KG];
     const u32x4 zero = {0u, 0u, 0u, 0u};
     const bf16* zb = z + (size_t)bidx * NN * D;
@@ -352,14 +346,38 @@ __global__ __launch_bounds__(256, 2) void k1_project_fold(
         const bool live = (m & 31) < kvalid;
         const bf16* zp = zb + (live ? zpair(m) : 0) * D;
 #pragma unroll
-        for (int kg = 0; kg < KG; ++kg) zf[rb][kg] = live ? ld16(zp + (kg * 4 + g4) * 8) : zero;
+        for (int kg = 0; kg < KG; ++kg) {
+            const u32x4 v = ld16(zp + (kg * 4 + g4) * 8);
+            zf[rb][kg] = live ? v : zero;
+        }
     }
+    // Without a mask the load reads z (any valid address) and is discarded, so
+    // the load is not behind a branch either.
     float mval[RB];
+    const bf16* mb = mask ? mask + (size_t)bidx * NN : zb;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         const int m = rb * 16 + l16;
-        mval[rb] = (m & 31) < kvalid ? (mask ? (float)mask[(size_t)bidx * NN + zpair(m)] : 1.0f) : 0.0f;
+        const bool live = (m & 31) < kvalid;
+        const float mv = (float)mb[live ? zpair(m) : 0];
+        mval[rb] = live ? (mask ? mv : 1.0f) : 0.0f;
     }
+    {
+        // Correction rows: 4C entries of 16 bytes, C/16 kilobytes.
+        const uint32_t lds_ext = lds_addr_of(ext);
+        for (int q = wave_s; q < C / 16; q += NWV)
+            dma16_to_lds(Xf + (size_t)q * 512 + lane * 8, lds_ext + (uint32_t)(q * 1024));
+    }
+    // Older than the DMA of stages 1 and 2, so the prologue's wait for stage 0
+    // covers every load above.
+    issue(0, ring);
+    issue(1, ring + STAGE);
+    issue(2, ring + 2 * STAGE);   // NQ = C / 8 >= 4
+    if (wave == 0)
+#pragma unroll
+        for (int i = 0; i < RB * 16 * 16 / (64 * 16); ++i)
+            *reinterpret_cast<u32x4*>(xfa + NWV * RB * 256 + (i * 64 + lane) * 16) = u32x4{0u, 0u, 0u, 0u};
+
     const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
