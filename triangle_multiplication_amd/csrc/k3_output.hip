@@ -18,7 +18,6 @@
 #include "trimul_device.hpp"
 #include "trimul_launch.hpp"
 
-
 namespace trimul {
 
 template <typename T, int D, int C>
@@ -299,7 +298,6 @@ template <> struct OFrags<4> {
     }
 };
 #undef TRIMUL_TR2
-
 
 template <int D, int C>
 __global__ __launch_bounds__(512) void k3_output_fold(
