@@ -365,6 +365,28 @@ def test_workload_out_bf16_b1_n4096_d256(tb):
     _run_workload(tb, "out_bf16_b1_n4096_d256", "outgoing")
 
 
+@pytest.mark.parametrize("direction", ["outgoing", "incoming"])
+def test_fwd_ragged_large_tailmask(tb, direction):
+    # The large-N kernels on a ragged size: N = 2056 leaves an 8-token k block
+    # in the projection and contraction and an 8-row tile edge in the
+    # contraction; the last floor(N/10) = 205 tokens are masked, so the mask
+    # boundary (token 1851) falls inside a k block.  D = C = 256 selects the
+    # folded projection and output kernels.
+    wl = inputs.Workload("ragged_bf16_b1_n2056_d256_tailmask", "bf16", (direction,), 1, 2056, 256, 256,
+                         mask="tail10", check="grid")
+    say("ragged large", direction)
+    z, mask, w = workload_inputs(wl)
+    layer = _layer(tb, w, "bf16")
+    out = layer.forward(z, mask, direction)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    err = oracle_check(z, mask, w, direction, out, full=False, extra=wl.sample_extra())
+    say("  err", err)
+    assert err <= wl.tol
+    n_valid = 2056 - 205
+    assert (out[0, n_valid:, ::89] == 0).all() and (out[0, ::89, n_valid:] == 0).all()
+
+
 def test_workload_in_bf16_b1_n8192_d128_chains(tb):
     z, mask, w, layer, out = _run_workload(tb, "in_bf16_b1_n8192_d128_chains", "incoming")
     # padded tail rows and columns are exactly zero (beta_out = 0)
