@@ -220,11 +220,12 @@ __global__ __launch_bounds__(256) void k3_output(
 // v_dot2_f32_bf16 (sum and sum of squares, var = E[v^2] - mu^2 in fp32).
 // The epilogue is then out = (rstd_o acc_p) / (1 + 2^(-log2(e) rstd_x acc_g)).
 //
-// One 512-thread workgroup per CU walks 32-pair tiles; the two halves of each
-// 64-pair run go to the same CU back to back, so the second half of every
-// 128-byte line of o is an L2 hit.  Each of the 8 waves owns 16-row blocks
-// rb = wave + 8 r of the D output channels and holds those rows of W'_g and
-// W'_p in registers for the whole kernel.  A ring of four LDS slots, filled by
+// Persistent workgroups (one of 8 waves per CU at D = 256, two of 4 waves at
+// D = 128) walk 32-pair tiles; the two halves of each 64-pair run go to the
+// same workgroup back to back, so the second half of every 128-byte line of o
+// is an L2 hit.  Each wave owns two 16-row blocks of the D output channels
+// (rows interleaved so that a lane's results are eight consecutive channels)
+// and holds those rows of W'_g and W'_p in registers for the whole kernel.  A ring of four LDS slots, filled by
 // global->LDS DMA three tiles ahead, holds per tile
 //   z: 32 rows of 2D bytes, 16-byte chunk c of row p stored at c ^ (p % 16);
 //   o: C channel rows of 64 bytes (32 pairs), 32-byte half h of row c stored at
@@ -235,12 +236,16 @@ __global__ __launch_bounds__(256) void k3_output(
 // waves run the MFMAs and the epilogue of tile t; one barrier ends the tile.
 // ---------------------------------------------------------------------------
 namespace k3f {
-constexpr int TM = 32, NB = TM / 16, NW = 8, NS = 4;
+constexpr int TM = 32, NB = TM / 16, NS = 4;
+// Waves per workgroup: 8 at D = 256 (one workgroup per CU), 4 at D = 128
+// (two per CU), so that every wave owns two paired 16-row blocks.
+constexpr int waves_for(int D) { return D >= 256 ? 8 : 4; }
 constexpr float LOG2E = 1.4426950408889634f;
 
 template <int D, int C>
 struct Cfg {
     static constexpr int KGD = D / 32, KGC = C / 32;
+    static constexpr int NW = waves_for(D);
     static constexpr int RBT = D / 16, RBW = RBT / NW;      // 16-row output blocks (per wave)
     static constexpr int ZB = TM * D * 2, OB = C * TM * 2;   // slot bytes of z and of o
     static constexpr int SLOT = ZB + OB;
@@ -300,7 +305,7 @@ template <> struct OFrags<4> {
 #undef TRIMUL_TR2
 
 template <int D, int C>
-__global__ __launch_bounds__(512) void k3_output_fold(
+__global__ __launch_bounds__(k3f::waves_for(D) * 64) void k3_output_fold(
     const bf16* __restrict__ z, const bf16* __restrict__ o, const bf16* __restrict__ Wg,
     const bf16* __restrict__ Wp, const bf16* __restrict__ Xg, const bf16* __restrict__ Xp,
     float eps, bf16* __restrict__ out, int N, int n_super)
@@ -308,7 +313,7 @@ __global__ __launch_bounds__(512) void k3_output_fold(
     using namespace k3f;
     using Cf = Cfg<D, C>;
     constexpr int KGD = Cf::KGD, KGC = Cf::KGC, RBW = Cf::RBW;
-    constexpr int ZB = Cf::ZB, SLOT = Cf::SLOT, FRAG = Cf::FRAG, STAT = Cf::STAT;
+    constexpr int ZB = Cf::ZB, SLOT = Cf::SLOT, FRAG = Cf::FRAG, STAT = Cf::STAT, NW = Cf::NW;
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     __shared__ __attribute__((aligned(1024))) unsigned char smem[Cf::LDS];
     unsigned char* ring = smem;
@@ -556,8 +561,10 @@ static hipError_t launch_k3_fold(const Params& p, const void* z, const void* o, 
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess)
         (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    const long long grid = n_super < cus ? n_super : cus;
-    hipLaunchKernelGGL((k3_output_fold<D, C>), dim3((unsigned)grid), dim3(512), 0, s, (const bf16*)z,
+    constexpr int NW = k3f::Cfg<D, C>::NW;
+    const long long slots = (long long)cus * (8 / NW);       // workgroups resident at once
+    const long long grid = n_super < slots ? n_super : slots;
+    hipLaunchKernelGGL((k3_output_fold<D, C>), dim3((unsigned)grid), dim3(NW * 64), 0, s, (const bf16*)z,
                        (const bf16*)o, (const bf16*)p.w_gout_f, (const bf16*)p.w_pout_f,
                        (const bf16*)p.x_gout, (const bf16*)p.x_pout, p.eps, (bf16*)out, N,
                        (int)n_super);
