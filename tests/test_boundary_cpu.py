@@ -154,3 +154,54 @@ def test_product_path_does_not_reference_the_oracle():
             text = open(f).read()
             assert "import oracle" not in text and "from oracle" not in text, f
             assert "orc_" not in text and "liborc" not in text, f
+
+
+def _unbound_layer(D=32, C=32, dtype="bf16"):
+    """A TriMul whose tensors live on the CPU and that has no handle: any call
+    that got past the Python checks would reach the C library with a NULL
+    handle and raise TriMulError, so a ValueError proves the check came first."""
+    import torch
+    layer = tb.TriMul.__new__(tb.TriMul)
+    layer.dtype, layer.tdtype = dtype, {"bf16": torch.bfloat16, "fp32": torch.float32}[dtype]
+    layer.D, layer.C, layer.h, layer._ws = D, C, None, None
+    layer.device_type = "cpu"
+    return layer
+
+
+@pytest.mark.parametrize("bad", ["shape", "dtype", "strided", "small"])
+def test_forward_rejects_bad_out_before_enqueueing(bad):
+    import torch
+    layer = _unbound_layer()
+    z = torch.zeros((1, 8, 8, 32), dtype=torch.bfloat16)
+    out = {"shape": torch.empty((1, 8, 8, 64), dtype=torch.bfloat16),
+           "dtype": torch.empty((1, 8, 8, 32), dtype=torch.float32),
+           "strided": torch.empty((1, 8, 8, 64), dtype=torch.bfloat16)[..., ::2],
+           "small": torch.empty((1, 8, 4, 32), dtype=torch.bfloat16)}[bad]
+    with pytest.raises(ValueError) as e:
+        layer.forward(z, None, "outgoing", out=out)
+    assert "out must be" in str(e.value)
+
+
+def test_forward_checks_reach_the_library_when_arguments_are_good():
+    import torch
+    layer = _unbound_layer()
+    z = torch.zeros((1, 8, 8, 32), dtype=torch.bfloat16)
+    with pytest.raises(tb.TriMulError) as e:   # NULL handle: the C side refuses it
+        layer.forward(z, None, "outgoing", out=torch.empty_like(z))
+    assert e.value.status == tb.TRIMUL_ERR_INVALID_ARG
+
+
+def test_stage_helpers_check_shapes():
+    import torch
+    layer = _unbound_layer(32, 64)
+    good = torch.zeros(tb.ab_storage_shape("bf16", 1, 64, 16), dtype=torch.bfloat16)
+    with pytest.raises(ValueError) as e:
+        layer.contract(good, torch.zeros((1, 64, 16, 16), dtype=torch.bfloat16))
+    assert "b_cm" in str(e.value)
+    z = torch.zeros((1, 16, 16, 32), dtype=torch.bfloat16)
+    with pytest.raises(ValueError) as e:
+        layer.output(z, torch.zeros((1, 32, 16, 16), dtype=torch.bfloat16))
+    assert "o must be" in str(e.value)
+    with pytest.raises(ValueError) as e:
+        layer.project(z, torch.zeros((1, 16, 8), dtype=torch.bfloat16))
+    assert "mask" in str(e.value)

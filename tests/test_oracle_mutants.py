@@ -41,3 +41,25 @@ def test_pins_catch_mutant(name, tmp_path):
                         os.path.join(ROOT, "tests", "test_oracle_pins.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, "pins did not catch mutant %s:\n%s" % (name, r.stdout[-2000:])
+
+
+# The hand-worked examples (tests/golden) alone, without any test that recomposes
+# the formula from library routines, catch every planted mistake a no-mask
+# example can see (b_unmasked needs a mask; the other pins catch it).
+VALUE_PINNED = sorted(set(MUTANTS) - {"b_unmasked"})
+
+
+@pytest.mark.parametrize("name", VALUE_PINNED)
+def test_hand_worked_values_catch_mutant(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    msrc = tmp_path / "mutant.c"
+    msrc.write_text(src.replace(old, new, 1))
+    lib = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-o", str(lib),
+                    str(msrc), "-lm"], check=True)
+    env = dict(os.environ, TRIMUL_ORACLE_LIB=str(lib), OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-p", "no:cacheprovider",
+                        "-k", "hand_worked", os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, "hand-worked values did not catch mutant %s:\n%s" % (name, r.stdout[-2000:])

@@ -149,6 +149,36 @@ def test_hand_worked_example(direction):
     np.testing.assert_allclose(r["out"][0], out, rtol=1e-14, atol=1e-15)
 
 
+def _golden_affine_out():
+    with open(os.path.join(GOLDEN, "hand_n2_d2_c2_affine_out.json")) as f:
+        return json.load(f)
+
+
+@pytest.mark.parametrize("direction", ["outgoing", "incoming"])
+def test_hand_worked_example_affine_output(direction):
+    """Values derived by hand (derivation in the fixture) with gamma_out != gamma_in,
+    beta_out != 0 and non-symmetric p_out and g_out: pins the output LayerNorm's own
+    parameters and the [out][in] orientation of both output matrices."""
+    g = _golden_affine_out()
+    f32 = lambda k: np.asarray(g[k], np.float32)
+    w = inputs.TriMulWeights(f32("ln_in_w"), f32("ln_in_b"), f32("p_in"), f32("g_in"),
+                             f32("ln_out_w"), f32("ln_out_b"), f32("p_out"), f32("g_out"),
+                             g["eps"])
+    out = oracle.trimul_full(f32("z"), None, w, direction)
+    eps = g["eps"]
+    sg = lambda t: 1.0 / (1.0 + math.exp(-t))
+    rho = (1.0 + eps) ** -0.5
+    kappa = (rho ** 2 / 2) / math.sqrt(rho ** 4 / 4 + eps)
+    S = np.asarray(g["S"])
+    t = np.asarray(g["t_outgoing"] if direction == "outgoing" else g["t_incoming"])
+    ref = np.empty((2, 2, 2))
+    for i in range(2):
+        for j in range(2):
+            s, tk = S[i, j], t[i, j] * kappa
+            ref[i, j] = (tk / 2 * sg(s * rho), (-8 * tk - 2.5) * sg(0.75 * s * rho))
+    np.testing.assert_allclose(out[0], ref, rtol=1e-13, atol=1e-14)
+
+
 # ----------------------------------------------------------------------------
 # P2: constant z
 # ----------------------------------------------------------------------------

@@ -180,6 +180,9 @@ class TriMul:
     on, in the handle's dtype.
     """
 
+    # Device type every tensor argument must live on.
+    device_type = "cuda"
+
     def __init__(self, weights, dtype="bf16"):
         import torch
         self.dtype = dtype
@@ -197,18 +200,29 @@ class TriMul:
             self._ws = torch.empty(need, dtype=torch.uint8, device=device)
         return self._ws
 
-    def _check_tensor(self, t, name, shape):
-        if t.dtype != self.tdtype or not t.is_contiguous() or not t.is_cuda or tuple(t.shape) != shape:
-            raise ValueError("%s must be a contiguous %s device tensor of shape %s; got %s %s %s"
-                             % (name, self.tdtype, shape, t.dtype, tuple(t.shape), t.device))
+    def _check_tensor(self, t, name, shape, device=None):
+        """Raise ValueError unless t is a contiguous tensor of the handle's dtype
+        with exactly ``shape``, on this layer's device type (and on ``device``
+        if given).  The kernels index every tensor as dense row-major with the
+        sizes the shape implies, so anything else must be refused here."""
+        if (t.dtype != self.tdtype or not t.is_contiguous() or t.device.type != self.device_type
+                or tuple(t.shape) != tuple(shape) or (device is not None and t.device != device)):
+            raise ValueError("%s must be a contiguous %s %s tensor of shape %s%s; got %s %s on %s%s"
+                             % (name, self.tdtype, self.device_type, tuple(shape),
+                                "" if device is None else " on " + str(device), t.dtype,
+                                tuple(t.shape), t.device, "" if t.is_contiguous() else " (strided)"))
 
     def forward(self, z, mask=None, direction="outgoing", out=None, stream=None):
         import torch
+        if z.dim() != 4:
+            raise ValueError("z must be [B, N, N, D]; got shape %s" % (tuple(z.shape),))
         B, N = int(z.shape[0]), int(z.shape[1])
         self._check_tensor(z, "z", (B, N, N, self.D))
         if mask is not None:
-            self._check_tensor(mask, "mask", (B, N, N))
-        if out is None:
+            self._check_tensor(mask, "mask", (B, N, N), z.device)
+        if out is not None:
+            self._check_tensor(out, "out", (B, N, N, self.D), z.device)
+        else:
             out = torch.empty_like(z)
         ws = self.workspace(B, N, z.device)
         trimul_fwd(self.h, z, mask, direction, out, ws, stream)
@@ -219,6 +233,9 @@ class TriMul:
     def project(self, z, mask=None, direction="outgoing"):
         import torch
         B, N = int(z.shape[0]), int(z.shape[1])
+        self._check_tensor(z, "z", (B, N, N, self.D))
+        if mask is not None:
+            self._check_tensor(mask, "mask", (B, N, N), z.device)
         a = torch.empty(ab_storage_shape(self.dtype, B, self.C, N), dtype=self.tdtype, device=z.device)
         b = torch.empty_like(a)
         trimul_internal_project(self.h, z, mask, direction, a, b)
@@ -227,12 +244,18 @@ class TriMul:
     def contract(self, a_cm, b_cm):
         import torch
         B, N = int(a_cm.shape[0]), int(a_cm.shape[-2])
+        shape = ab_storage_shape(self.dtype, B, self.C, N)
+        self._check_tensor(a_cm, "a_cm", shape)
+        self._check_tensor(b_cm, "b_cm", shape, a_cm.device)
         o = torch.empty((B, self.C, N, N), dtype=self.tdtype, device=a_cm.device)
         trimul_internal_contract(self.h, a_cm, b_cm, o)
         return o
 
     def output(self, z, o):
         import torch
+        B, N = int(z.shape[0]), int(z.shape[1])
+        self._check_tensor(z, "z", (B, N, N, self.D))
+        self._check_tensor(o, "o", (B, self.C, N, N), z.device)
         out = torch.empty_like(z)
         trimul_internal_output(self.h, z, o, out)
         return out

@@ -216,8 +216,7 @@ WORKLOADS = {
                                                  ("outgoing", "incoming"), 1, 384, 128, 128,
                                                  mask="tail10"),
     "outin_bf16_b2_n1024_d128": Workload("outin_bf16_b2_n1024_d128", "bf16",
-                                         ("outgoing", "incoming"), 2, 1024, 128, 128,
-                                         check="grid"),
+                                         ("outgoing", "incoming"), 2, 1024, 128, 128),
     "out_bf16_b1_n4096_d256": Workload("out_bf16_b1_n4096_d256", "bf16", ("outgoing",),
                                        1, 4096, 256, 256, check="grid"),
     "in_bf16_b1_n8192_d128_chains": Workload("in_bf16_b1_n8192_d128_chains", "bf16",
