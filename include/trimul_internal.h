@@ -34,13 +34,36 @@ trimul_status trimul_internal_project(trimul_handle *h, const void *z, const voi
                                       hipStream_t stream);
 
 /*
+ * The mask table of a masked bf16 contraction: int32 [mask_table_ints] with
+ * T = ceil(N/256) row tiles, mask_table_ints = 2 B T + 4 + B T^2:
+ *   [0, 2BT)          ranges[b][t] = (lo, hi) in steps of 32 keys such that for
+ *                     every row r of tile t and every key k outside
+ *                     [32 lo, 32 hi), M[r][k] == 0, with M[r][k] = mask[b][r][k]
+ *                     (outgoing) or mask[b][k][r] (incoming); lo is the first
+ *                     live key's step, hi one past the last one's; (0, 0) when
+ *                     no key is live;
+ *   [2BT, 2BT + 4)    header ([0]: live tile pairs of the fullest batch);
+ *   [2BT + 4, ...)    per batch, its T^2 tile pairs (ti | tj << 16), pairs with
+ *                     a live key step first.
+ * mask_ranges fills the ranges and clears the header (the scan trimul_fwd runs
+ * before a masked bf16 contraction); pair_mask and table 16-byte aligned.
+ */
+trimul_status trimul_internal_mask_ranges(trimul_handle *h, const void *pair_mask, int B, int N,
+                                          trimul_direction dir, int *table, hipStream_t stream);
+
+/*
  * Triangle contraction, C*B independent N x N x N products with fp32
  * accumulation: o[b][c][i][j] = sum_k A[b][c](i, k) * B[b][c](j, k), rounded
  * once to the dtype.  a_cm, b_cm in the storage described above; o: plain
- * [B][C][N][N].
+ * [B][C][N][N].  table: NULL, or a mask table whose ranges were filled by
+ * trimul_internal_mask_ranges (bf16 only): the pair lists are built, then the
+ * kernel runs only the key steps inside both row tiles' ranges, which must
+ * hold every key where A or B can be nonzero.  dir selects only which of the
+ * handle's plans is used, (B, N, dir, masked = table != NULL).
  */
 trimul_status trimul_internal_contract(trimul_handle *h, const void *a_cm, const void *b_cm,
-                                       int B, int N, void *o, hipStream_t stream);
+                                       int *table, int B, int N, trimul_direction dir, void *o,
+                                       hipStream_t stream);
 
 /*
  * Output stage: out[b][i][j][:] = (p_out LayerNorm_out(o[b][:][i][j]))
@@ -49,6 +72,31 @@ trimul_status trimul_internal_contract(trimul_handle *h, const void *a_cm, const
  */
 trimul_status trimul_internal_output(trimul_handle *h, const void *z, const void *o, int B,
                                      int N, void *out, hipStream_t stream);
+
+/*
+ * Plans (see trimul_tune).  set_plan records a plan for a call shape in the
+ * handle (as trimul_tune does, without timing or writing the cache), so tests
+ * can run every candidate; get_plan returns the plan trimul_fwd would use.
+ * plan_candidates writes up to cap candidates and returns how many exist.
+ */
+trimul_status trimul_internal_set_plan(trimul_handle *h, int B, int N, trimul_direction dir,
+                                       int masked, int k2_order, int k2_gm);
+trimul_status trimul_internal_get_plan(trimul_handle *h, int B, int N, trimul_direction dir,
+                                       int masked, int *k2_order, int *k2_gm);
+int trimul_internal_plan_candidates(int *k2_order, int *k2_gm, int cap);
+
+/*
+ * The plan cache file, host only (no device needed): store one entry
+ * (replacing the entry with the same key), look one up (returns 1 and fills
+ * the plan if found, 0 if not, -1 if the file cannot be read), and the path
+ * the library uses (written to buf, length returned; 0 when disabled).
+ */
+trimul_status trimul_internal_cache_store(const char *path, const char *device, int D, int C,
+                                          int dtype, int B, int N, int dir, int masked,
+                                          int k2_order, int k2_gm, double ms);
+int trimul_internal_cache_lookup(const char *path, const char *device, int D, int C, int dtype,
+                                 int B, int N, int dir, int masked, int *k2_order, int *k2_gm);
+int trimul_internal_cache_path(char *buf, int cap);
 
 #ifdef __cplusplus
 }

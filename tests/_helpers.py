@@ -57,3 +57,34 @@ def oracle_check(z, mask, w, direction, out, full=True, n_sample=64, extra=()):
         worst_num = max(worst_num, float(np.abs(got - ref).max()))
         worst_den = max(worst_den, float(np.abs(ref).max()))
     return worst_num / (worst_den if worst_den > 0 else 1.0)
+
+
+def _to_ab_storage(x, dtype):
+    """Plain [B, C, N, N] (row, k) tensor -> the stage buffers' storage
+    (include/trimul_internal.h): bf16 K-blocked [B, C, Kp/32, N, 32] with the
+    k >= N padding filled with NaN (never read), fp32 unchanged."""
+    if dtype != "bf16":
+        return x.contiguous()
+    B, C, N, _ = x.shape
+    kp = (N + 31) // 32 * 32
+    xp = torch.full((B, C, N, kp), float("nan"), dtype=x.dtype, device=x.device)
+    xp[..., :N] = x
+    return xp.view(B, C, N, kp // 32, 32).permute(0, 1, 3, 2, 4).contiguous()
+
+
+def _from_ab_storage(x, dtype):
+    """Inverse of _to_ab_storage: storage -> plain [B, C, N, N]."""
+    if dtype != "bf16":
+        return x
+    B, C, nb, N, _ = x.shape
+    return x.permute(0, 1, 3, 2, 4).reshape(B, C, N, nb * 32)[..., :N]
+
+
+def _exact_contract_reference(a, b, rows=None, chans=None):
+    """RNE-rounded exact integer sums sum_k a[c,i,k] b[c,j,k] in float64 on the device."""
+    A = a if chans is None else a[:, chans]
+    Bm = b if chans is None else b[:, chans]
+    if rows is not None:
+        A = A[:, :, rows]
+    ref = torch.matmul(A.double(), Bm.double().transpose(-1, -2).contiguous())
+    return ref

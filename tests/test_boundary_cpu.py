@@ -61,18 +61,23 @@ def test_arch_gate_null():
 
 def test_workspace_query_sizes():
     # a and b: B*C*N*Kp elements (bf16: Kp = N rounded up to 32; fp32: Kp = N),
-    # o: B*C*N*N elements; each rounded up to 256 bytes
+    # o: B*C*N*N elements, the mask table (int32);
+    # each rounded up to 256 bytes
     def r256(x):
         return (x + 255) // 256 * 256
-    assert tb.trimul_workspace_query(256, 256, "bf16", 1, 4096) == 3 * 256 * 4096 * 4096 * 2
-    assert tb.trimul_workspace_query(32, 32, "fp32", 1, 64) == 3 * 32 * 64 * 64 * 4
+
+    def rt(B, N):   # the mask table: ranges [B][T][2], 4-int header, pair lists [B][T*T]
+        T = (N + 255) // 256
+        return r256(4 * (2 * B * T + 4 + B * T * T))
+    assert tb.trimul_workspace_query(256, 256, "bf16", 1, 4096) == 3 * 256 * 4096 * 4096 * 2 + rt(1, 4096)
+    assert tb.trimul_workspace_query(32, 32, "fp32", 1, 64) == 3 * 32 * 64 * 64 * 4 + rt(1, 64)
     n = tb.trimul_workspace_query(32, 64, "bf16", 3, 8)
-    assert n == 2 * r256(3 * 64 * 8 * 32 * 2) + r256(3 * 64 * 8 * 8 * 2)
+    assert n == 2 * r256(3 * 64 * 8 * 32 * 2) + r256(3 * 64 * 8 * 8 * 2) + rt(3, 8)
     n = tb.trimul_workspace_query(64, 32, "bf16", 2, 200)
-    assert n == 2 * r256(2 * 32 * 200 * 224 * 2) + r256(2 * 32 * 200 * 200 * 2)
+    assert n == 2 * r256(2 * 32 * 200 * 224 * 2) + r256(2 * 32 * 200 * 200 * 2) + rt(2, 200)
     n = tb.trimul_workspace_query(64, 32, "fp32", 2, 200)
-    assert n == 3 * r256(2 * 32 * 200 * 200 * 4)
-    assert tb.trimul_workspace_query(128, 128, "bf16", 1, 8192) == 3 * 128 * 8192 ** 2 * 2
+    assert n == 3 * r256(2 * 32 * 200 * 200 * 4) + rt(2, 200)
+    assert tb.trimul_workspace_query(128, 128, "bf16", 1, 8192) == 3 * 128 * 8192 ** 2 * 2 + rt(1, 8192)
 
 
 def test_ab_storage_shape():

@@ -33,8 +33,12 @@ DIRECTIONS = {"outgoing": TRIMUL_OUTGOING, "incoming": TRIMUL_INCOMING,
               0: TRIMUL_OUTGOING, 1: TRIMUL_INCOMING}
 
 EXPORTED = ["trimul_create", "trimul_destroy", "trimul_workspace_size", "trimul_workspace_query",
-            "trimul_fwd", "trimul_check_arch", "trimul_status_string", "trimul_last_error",
-            "trimul_internal_project", "trimul_internal_contract", "trimul_internal_output"]
+            "trimul_workspace_size_lean", "trimul_fwd", "trimul_tune", "trimul_check_arch",
+            "trimul_status_string", "trimul_last_error",
+            "trimul_internal_project", "trimul_internal_mask_ranges", "trimul_internal_contract",
+            "trimul_internal_output", "trimul_internal_set_plan", "trimul_internal_get_plan",
+            "trimul_internal_plan_candidates", "trimul_internal_cache_store",
+            "trimul_internal_cache_lookup", "trimul_internal_cache_path"]
 
 
 class trimul_weights(ctypes.Structure):
@@ -52,8 +56,12 @@ _lib.trimul_workspace_size.argtypes = [_vp, _ci, _ci, ctypes.POINTER(_sz)]
 _lib.trimul_workspace_size.restype = _ci
 _lib.trimul_workspace_query.argtypes = [_ci, _ci, _ci, _ci, _ci, ctypes.POINTER(_sz)]
 _lib.trimul_workspace_query.restype = _ci
+_lib.trimul_workspace_size_lean.argtypes = [_vp, _ci, _ci, ctypes.POINTER(_sz)]
+_lib.trimul_workspace_size_lean.restype = _ci
 _lib.trimul_fwd.argtypes = [_vp, _vp, _vp, _ci, _ci, _ci, _vp, _vp, _sz, _vp]
 _lib.trimul_fwd.restype = _ci
+_lib.trimul_tune.argtypes = [_vp, _vp, _vp, _ci, _ci, _ci, _vp, _vp, _sz, _vp]
+_lib.trimul_tune.restype = _ci
 _lib.trimul_check_arch.argtypes = [ctypes.c_char_p]
 _lib.trimul_check_arch.restype = _ci
 _lib.trimul_status_string.argtypes = [_ci]
@@ -62,10 +70,25 @@ _lib.trimul_last_error.argtypes = []
 _lib.trimul_last_error.restype = ctypes.c_char_p
 _lib.trimul_internal_project.argtypes = [_vp, _vp, _vp, _ci, _ci, _ci, _vp, _vp, _vp]
 _lib.trimul_internal_project.restype = _ci
-_lib.trimul_internal_contract.argtypes = [_vp, _vp, _vp, _ci, _ci, _vp, _vp]
+_lib.trimul_internal_mask_ranges.argtypes = [_vp, _vp, _ci, _ci, _ci, _vp, _vp]
+_lib.trimul_internal_mask_ranges.restype = _ci
+_lib.trimul_internal_contract.argtypes = [_vp, _vp, _vp, _vp, _ci, _ci, _ci, _vp, _vp]
 _lib.trimul_internal_contract.restype = _ci
 _lib.trimul_internal_output.argtypes = [_vp, _vp, _vp, _ci, _ci, _vp, _vp]
 _lib.trimul_internal_output.restype = _ci
+_ip = ctypes.POINTER(_ci)
+_lib.trimul_internal_set_plan.argtypes = [_vp, _ci, _ci, _ci, _ci, _ci, _ci]
+_lib.trimul_internal_set_plan.restype = _ci
+_lib.trimul_internal_get_plan.argtypes = [_vp, _ci, _ci, _ci, _ci, _ip, _ip]
+_lib.trimul_internal_get_plan.restype = _ci
+_lib.trimul_internal_plan_candidates.argtypes = [_ip, _ip, _ci]
+_lib.trimul_internal_plan_candidates.restype = _ci
+_lib.trimul_internal_cache_store.argtypes = [ctypes.c_char_p, ctypes.c_char_p] + [_ci] * 9 + [ctypes.c_double]
+_lib.trimul_internal_cache_store.restype = _ci
+_lib.trimul_internal_cache_lookup.argtypes = [ctypes.c_char_p, ctypes.c_char_p] + [_ci] * 7 + [_ip, _ip]
+_lib.trimul_internal_cache_lookup.restype = _ci
+_lib.trimul_internal_cache_path.argtypes = [ctypes.c_char_p, _ci]
+_lib.trimul_internal_cache_path.restype = _ci
 
 
 class TriMulError(RuntimeError):
@@ -128,6 +151,12 @@ def trimul_workspace_size(h, B, N):
     return n.value
 
 
+def trimul_workspace_size_lean(h, B, N):
+    n = _sz(0)
+    _check(_lib.trimul_workspace_size_lean(h, B, N, ctypes.byref(n)))
+    return n.value
+
+
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -146,6 +175,80 @@ def trimul_fwd(h, z, mask, direction, out, workspace, stream=None):
                            _ptr(workspace), ws_bytes, _stream(stream)))
 
 
+def trimul_tune(h, z, mask, direction, out, workspace, stream=None):
+    """Time every candidate plan on these inputs, record the fastest, leave the
+    result in ``out`` (blocking)."""
+    B, N = int(z.shape[0]), int(z.shape[1])
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib.trimul_tune(h, _ptr(z), _ptr(mask), B, N, DIRECTIONS.get(direction, direction), _ptr(out),
+                            _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def trimul_internal_mask_ranges(h, mask, direction, table, stream=None):
+    B, N = int(mask.shape[0]), int(mask.shape[1])
+    _check(_lib.trimul_internal_mask_ranges(h, _ptr(mask), B, N, DIRECTIONS.get(direction, direction),
+                                            _ptr(table), _stream(stream)))
+
+
+def mask_table_ints(B, N):
+    """int32 length of the mask table (include/trimul_internal.h): ranges
+    [B][T][2], a 4-int header, pair lists [B][T*T], T = ceil(N/256)."""
+    T = (N + 255) // 256
+    return 2 * B * T + 4 + B * T * T
+
+
+def table_parts(table, B, N):
+    """Views (ranges [B][T][2], header [4], pairs [B][T*T]) of a mask table."""
+    T = (N + 255) // 256
+    r = table[:2 * B * T].view(B, T, 2)
+    hdr = table[2 * B * T:2 * B * T + 4]
+    pairs = table[2 * B * T + 4:2 * B * T + 4 + B * T * T].view(B, T * T)
+    return r, hdr, pairs
+
+
+def trimul_internal_set_plan(h, B, N, direction, masked, k2_order, k2_gm):
+    _check(_lib.trimul_internal_set_plan(h, B, N, DIRECTIONS.get(direction, direction), int(bool(masked)),
+                                         k2_order, k2_gm))
+
+
+def trimul_internal_get_plan(h, B, N, direction, masked):
+    o, g = _ci(0), _ci(0)
+    _check(_lib.trimul_internal_get_plan(h, B, N, DIRECTIONS.get(direction, direction), int(bool(masked)),
+                                         ctypes.byref(o), ctypes.byref(g)))
+    return o.value, g.value
+
+
+def plan_candidates():
+    n = _lib.trimul_internal_plan_candidates(None, None, 0)
+    o, g = (_ci * n)(), (_ci * n)()
+    _lib.trimul_internal_plan_candidates(o, g, n)
+    return [(o[i], g[i]) for i in range(n)]
+
+
+def cache_store(path, device, D, C, dtype, B, N, direction, masked, k2_order, k2_gm, ms):
+    _check(_lib.trimul_internal_cache_store(path.encode(), device.encode(), D, C, DTYPES.get(dtype, dtype), B, N,
+                                            DIRECTIONS.get(direction, direction), int(bool(masked)),
+                                            k2_order, k2_gm, float(ms)))
+
+
+def cache_lookup(path, device, D, C, dtype, B, N, direction, masked):
+    """(k2_order, k2_gm) recorded for the key, None if absent; raises OSError if unreadable."""
+    o, g = _ci(0), _ci(0)
+    r = _lib.trimul_internal_cache_lookup(path.encode(), device.encode(), D, C, DTYPES.get(dtype, dtype), B, N,
+                                          DIRECTIONS.get(direction, direction), int(bool(masked)),
+                                          ctypes.byref(o), ctypes.byref(g))
+    if r < 0:
+        raise OSError("plan cache %s cannot be read" % path)
+    return (o.value, g.value) if r else None
+
+
+def cache_path():
+    n = _lib.trimul_internal_cache_path(None, 0)
+    buf = ctypes.create_string_buffer(n + 1)
+    _lib.trimul_internal_cache_path(buf, n + 1)
+    return buf.value.decode()
+
+
 def trimul_internal_project(h, z, mask, direction, a_cm, b_cm, stream=None):
     B, N = int(z.shape[0]), int(z.shape[1])
     _check(_lib.trimul_internal_project(h, _ptr(z), _ptr(mask), B, N, DIRECTIONS.get(direction, direction),
@@ -161,10 +264,10 @@ def ab_storage_shape(dtype, B, C, N):
     return (B, C, N, N)
 
 
-def trimul_internal_contract(h, a_cm, b_cm, o, stream=None):
+def trimul_internal_contract(h, a_cm, b_cm, o, table=None, direction="outgoing", stream=None):
     B, N = int(o.shape[0]), int(o.shape[2])
-    _check(_lib.trimul_internal_contract(h, _ptr(a_cm), _ptr(b_cm), B, N, _ptr(o),
-                                         _stream(stream)))
+    _check(_lib.trimul_internal_contract(h, _ptr(a_cm), _ptr(b_cm), _ptr(table), B, N,
+                                         DIRECTIONS.get(direction, direction), _ptr(o), _stream(stream)))
 
 
 def trimul_internal_output(h, z, o, out, stream=None):
@@ -241,15 +344,44 @@ class TriMul:
         trimul_internal_project(self.h, z, mask, direction, a, b)
         return a, b
 
-    def contract(self, a_cm, b_cm):
+    def contract(self, a_cm, b_cm, table=None, direction="outgoing"):
         import torch
         B, N = int(a_cm.shape[0]), int(a_cm.shape[-2])
         shape = ab_storage_shape(self.dtype, B, self.C, N)
         self._check_tensor(a_cm, "a_cm", shape)
         self._check_tensor(b_cm, "b_cm", shape, a_cm.device)
+        if table is not None and (table.dtype != torch.int32 or not table.is_contiguous()
+                                  or tuple(table.shape) != (mask_table_ints(B, N),)
+                                  or table.device != a_cm.device):
+            raise ValueError("table must be a contiguous int32 tensor of %d elements on %s"
+                             % (mask_table_ints(B, N), a_cm.device))
         o = torch.empty((B, self.C, N, N), dtype=self.tdtype, device=a_cm.device)
-        trimul_internal_contract(self.h, a_cm, b_cm, o)
+        trimul_internal_contract(self.h, a_cm, b_cm, o, table, direction)
         return o
+
+    def mask_ranges(self, mask, direction="outgoing"):
+        """The mask table with its ranges filled (include/trimul_internal.h)."""
+        import torch
+        B, N = int(mask.shape[0]), int(mask.shape[1])
+        self._check_tensor(mask, "mask", (B, N, N))
+        t = torch.zeros(mask_table_ints(B, N), dtype=torch.int32, device=mask.device)
+        trimul_internal_mask_ranges(self.h, mask, direction, t)
+        return t
+
+    def tune(self, z, mask=None, direction="outgoing", out=None, stream=None):
+        """trimul_tune on these inputs; returns the output tensor."""
+        import torch
+        B, N = int(z.shape[0]), int(z.shape[1])
+        self._check_tensor(z, "z", (B, N, N, self.D))
+        if mask is not None:
+            self._check_tensor(mask, "mask", (B, N, N), z.device)
+        if out is not None:
+            self._check_tensor(out, "out", (B, N, N, self.D), z.device)
+        else:
+            out = torch.empty_like(z)
+        ws = self.workspace(B, N, z.device)
+        trimul_tune(self.h, z, mask, direction, out, ws, stream)
+        return out
 
     def output(self, z, o):
         import torch

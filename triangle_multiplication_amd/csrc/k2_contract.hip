@@ -23,7 +23,8 @@ namespace trimul {
 
 template <typename T, int BM, int BN>
 __global__ __launch_bounds__(256) void k2_contract(const T* __restrict__ A, const T* __restrict__ Bm,
-                                                   T* __restrict__ O, int N, int tiles_j)
+                                                   T* __restrict__ O, size_t o_stride, int bc0, int N,
+                                                   int tiles_j)
 {
     constexpr int CE = Elem<T>::CE;
     constexpr int KCH = 8;                  // 16-byte chunks per tile row per stage
@@ -56,9 +57,9 @@ __global__ __launch_bounds__(256) void k2_contract(const T* __restrict__ A, cons
     const int ti = first_i + (t % (GM * tiles_j)) % gm;
     const int tj = (t % (GM * tiles_j)) / gm;
     static_assert(sizeof(T) == 4, "bf16 operands are K-blocked and use k2_contract_ppp");
-    const T* Ab = A + bc * slab;
-    const T* Bb = Bm + bc * slab;
-    T* Ob = O + bc * slab;
+    const T* Ab = A + (bc0 + bc) * slab;
+    const T* Bb = Bm + (bc0 + bc) * slab;
+    T* Ob = O + bc * o_stride;
     auto opoff = [&](int row, int k) -> size_t { return (size_t)row * N + k; };
     const int i0 = ti * BM, j0 = tj * BN;
 
@@ -177,10 +178,16 @@ __device__ inline int slot_off(int row, int chunk)
 #define TRIMUL_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
 // Persistent kernel: one 512-thread workgroup per CU walks its tiles g, g + G,
-// ... in an XCD-banded order (workgroup g runs on XCD g % 8, each XCD gets a
-// compact band of tiles, walked in groups of GM row panels column by column,
-// so the ~32 tiles an XCD runs at once share K-slices of a few panels in its
-// L2; GM = 8 measured best against 1, 2, 4 and 16 at N = 4096).
+// ... in an XCD-aware order (workgroup g runs on XCD g % 8).  Two orders:
+//  order 0: the launch's tiles are cut into 8 contiguous bands, one per XCD;
+//  order 1: each round of G consecutive tiles (one per workgroup) is cut into
+//           8 contiguous blocks, one per XCD, so all XCDs work on the same few
+//           channels at once and what one XCD's L2 misses, the last-level
+//           cache (shared by all XCDs) still holds from the others.
+// Within a channel, tiles are walked in groups of gm row panels, column by
+// column, so the ~32 tiles an XCD runs at once share K-slices of a few panels
+// in its L2 (gm = 8 measured best against 1, 2, 4 and 16 at N = 4096 with
+// order 0).
 //
 // 8 waves in a 2 x 4 grid, each owning a 128 x 64 block of the tile (8 x 4
 // MFMA tiles, 128 accumulators per lane); the two waves that share a SIMD
@@ -210,14 +217,36 @@ __device__ inline int slot_off(int row, int chunk)
 // groups do this at the same point of their own phase sequence, so every wave
 // still executes the same barriers.
 //
+// Masked calls pass a table of live K-step ranges per row tile: a tile runs
+// only the K-steps where both its A rows and its B rows can be nonzero (every
+// skipped product is an exact zero, so the sums are unchanged); a tile with
+// no such step runs one step of zeros (the DMA is pushed out of range) and
+// stores its zeros.  Step counts per tile are the same for every wave of the
+// workgroup, so the barrier sequence stays uniform.  The table also lists each
+// batch's tile pairs live-first, and the launch's tiles are numbered so that
+// every channel's live pairs come before any dead pair: rounds of live tiles
+// then stay uniform and the workgroups of an XCD stay in step (a dead tile
+// among live ones lets its workgroup run ahead and stop sharing panels).
+//
 // Operands are K-blocked (kblk_off): a step's 256 rows of one operand are one
 // contiguous 16 KB run, and each DMA instruction reads one contiguous
 // kilobyte (16 rows x 64 bytes).  With row-major operands the same step reads
 // 256 half cache lines 2N bytes apart, which measured 12 % slower overall.
+struct K2PArgs {
+    const bf16* A;        // operand slabs [B*C][aslab], K-blocked
+    const bf16* Bm;
+    bf16* O;              // output of local slab t at O + t * o_stride
+    size_t o_stride;
+    const int* ranges;    // mask table: [B][tiles][2] live K-step ranges, or null
+    const int* hdr;       //   its header ([0] = live pairs of the fullest batch)
+    const unsigned* pairs;//   its pair lists [B][tiles^2]
+    int N, C, total;      // total = tiles of this launch (a multiple of 8)
+    int bc0;              // first operand slab of this launch
+    int order, gm;        // Plan
+};
+
 template <int NSP>
-__global__ __launch_bounds__(512) void k2_contract_ppp(const bf16* __restrict__ A,
-                                                       const bf16* __restrict__ Bm,
-                                                       bf16* __restrict__ O, int N, int total)
+__global__ __launch_bounds__(512) void k2_contract_ppp(K2PArgs args)
 {
     using namespace k2big;
     constexpr int NW = 8;
@@ -229,27 +258,63 @@ __global__ __launch_bounds__(512) void k2_contract_ppp(const bf16* __restrict__ 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 2, wn = wave & 3;        // group = wm
+    const int N = args.N, total = args.total;
     const size_t slab = (size_t)N * N;
     const int tiles = (N + BM - 1) / BM;
     const int per_bc = tiles * tiles;
     const int G = gridDim.x, g = blockIdx.x;
     const int n_my = (total - g + G - 1) / G;       // tiles of this workgroup (g < total)
     const int nk = (N + BK - 1) / BK;
-    const int S = n_my * nk;                        // steps of this workgroup (< 2^31)
 
-    // Tile tl of this workgroup: virtual block g + tl*G through the XCD-banded
-    // order, a bijection of [0, total) because total is a multiple of 8 (C is);
-    // with G a multiple of 8 every tile of workgroup g lies in g's band.
-    auto tile_geo = [&](int tl, size_t& bc, int& i0, int& j0) {
-        const unsigned vb = (unsigned)g + (unsigned)tl * (unsigned)G;
-        const unsigned logical = (vb & 7u) * ((unsigned)total >> 3) + (vb >> 3);
+    // Tile tl of this workgroup: virtual block vb = g + tl*G through the
+    // order's map, a bijection of [0, total) (total and G are multiples of 8),
+    // which keeps every tile of workgroup g on g's XCD.
+    auto logical_of = [&](unsigned vb) -> unsigned {
+        if (args.order == 0) return (vb & 7u) * ((unsigned)total >> 3) + (vb >> 3);
+        const unsigned r = vb / (unsigned)G, gg = vb - r * (unsigned)G;
+        const unsigned rem = (unsigned)total - r * (unsigned)G;
+        const unsigned R = rem < (unsigned)G ? rem : (unsigned)G;   // tiles of round r
+        return r * (unsigned)G + (gg & 7u) * (R >> 3) + (gg >> 3);
+    };
+    // Masked: the first nbc * nl logical tiles are slots [0, nl) of every
+    // slab's pair list, the rest slots [nl, tiles^2).
+    const unsigned nl = args.ranges ? (unsigned)args.hdr[0] : 0u;
+    const unsigned nbc_l = (unsigned)total / (unsigned)per_bc;
+    auto tile_geo = [&](int tl, size_t& bc, int& ti, int& tj) {
+        const unsigned logical = logical_of((unsigned)g + (unsigned)tl * (unsigned)G);
+        if (args.ranges) {
+            unsigned p;
+            if (logical < nbc_l * nl) {
+                bc = logical / nl;
+                p = logical % nl;
+            } else {
+                const unsigned r = logical - nbc_l * nl, nd = (unsigned)per_bc - nl;
+                bc = r / nd;
+                p = nl + r % nd;
+            }
+            const unsigned e = args.pairs[((size_t)args.bc0 + bc) / (size_t)args.C * per_bc + p];
+            ti = (int)(e & 0xffffu);
+            tj = (int)(e >> 16);
+            return;
+        }
         bc = logical / per_bc;
         const int t = (int)(logical % per_bc);
-        constexpr int GM = 8;
+        const int GM = args.gm;
         const int first_i = (t / (GM * tiles)) * GM;
         const int gm = min(GM, tiles - first_i);
-        i0 = (first_i + (t % (GM * tiles)) % gm) * BM;
-        j0 = ((t % (GM * tiles)) / gm) * BN;
+        ti = first_i + (t % (GM * tiles)) % gm;
+        tj = (t % (GM * tiles)) / gm;
+    };
+    // K-steps of tile (bc, ti, tj): [klo, klo + kn); kn >= 1, and dead tiles
+    // (no live step) run one step that reads zeros.
+    auto krange = [&](size_t bc, int ti, int tj, int& klo, int& kn, bool& live) {
+        if (!args.ranges) { klo = 0; kn = nk; live = true; return; }
+        const int b = (int)(((size_t)args.bc0 + bc) / (size_t)args.C);
+        const int* r = args.ranges + (size_t)b * tiles * 2;
+        const int lo = max(r[2 * ti], r[2 * tj]), hi = min(r[2 * ti + 1], r[2 * tj + 1]);
+        live = lo < hi;
+        klo = live ? lo : 0;
+        kn = live ? hi - lo : 1;
     };
 
     // Operand slab: [nk][N][32] bf16.  DMA instruction q of a wave covers rows
@@ -272,29 +337,35 @@ __global__ __launch_bounds__(512) void k2_contract_ppp(const bf16* __restrict__ 
     static_assert(DPO == 2, "B row permutation assumes two DMA instructions per operand per wave");
     const unsigned lane_off_b = (unsigned)(32 * wave + 8 * (dr >> 2) + (dr & 3)) * ROWB + dc * 16u;
 
-    // DMA cursor: the next step to load is K-step ikk of tile itl.  The tile's
-    // buffer descriptors and row offsets are recomputed only when the cursor
-    // enters a new tile; past the workgroup's last tile (and for K-chunks past
-    // N) the offset is pushed beyond the buffer's range, so the DMA reads zeros.
-    int itl = 0, ikk = 0;
+    // DMA cursor: the next step to load is step ikk of tile itl (K-step
+    // iklo + ikk).  The tile's buffer descriptors, row offsets and K range are
+    // recomputed only when the cursor enters a new tile; past the workgroup's
+    // last tile, in dead tiles and for K-chunks past N the offset is pushed
+    // beyond the buffer's range, so the DMA reads zeros.
+    int itl = 0, ikk = 0, iklo = 0, ikn = 1;
     __amdgpu_buffer_rsrc_t ra, rb;
     unsigned oa_t = 0, ob_t = 0;
     bool ilive = true;
     auto set_tile = [&]() {
-        ilive = itl < n_my;
-        size_t bc; int i0, j0;
-        tile_geo(ilive ? itl : 0, bc, i0, j0);
-        ra = __builtin_amdgcn_make_buffer_rsrc((void*)(A + bc * aslab), 0, nrec, 0x00020000);
-        rb = __builtin_amdgcn_make_buffer_rsrc((void*)(Bm + bc * aslab), 0, nrec, 0x00020000);
-        oa_t = lane_off + (unsigned)i0 * ROWB;
-        ob_t = lane_off_b + (unsigned)j0 * ROWB;
+        const bool have = itl < n_my;
+        size_t bc; int ti, tj;
+        tile_geo(have ? itl : 0, bc, ti, tj);
+        bool klive;
+        krange(bc, ti, tj, iklo, ikn, klive);
+        ilive = have && klive;
+        const size_t sb = (size_t)args.bc0 + bc;
+        ra = __builtin_amdgcn_make_buffer_rsrc((void*)(args.A + sb * aslab), 0, nrec, 0x00020000);
+        rb = __builtin_amdgcn_make_buffer_rsrc((void*)(args.Bm + sb * aslab), 0, nrec, 0x00020000);
+        oa_t = lane_off + (unsigned)(ti * BM) * ROWB;
+        ob_t = lane_off_b + (unsigned)(tj * BN) * ROWB;
     };
     set_tile();
     int isl = 0;                                    // ring slot of the next step
     auto issue = [&]() {
         unsigned char* st = smem + isl * STB + wave * DPO * 1024;
-        const int k0 = ikk * BK;
-        const unsigned kb = (unsigned)ikk * kstride;
+        const int kk = iklo + ikk;
+        const int k0 = kk * BK;
+        const unsigned kb = (unsigned)kk * kstride;
         const unsigned kpen = (ilive && k0 + dc * 8 < N) ? 0u : 0x80000000u;
 #pragma unroll
         for (int q = 0; q < DPO; ++q) {
@@ -304,7 +375,7 @@ __global__ __launch_bounds__(512) void k2_contract_ppp(const bf16* __restrict__ 
                                                      (ob_t + q * 4u * ROWB + kb) | kpen, 0, 0, 0);
         }
         if (++isl == NSP) isl = 0;
-        if (++ikk == nk) { ikk = 0; ++itl; set_tile(); }
+        if (++ikk == ikn) { ikk = 0; ++itl; set_tile(); }
     };
 
     const int rchunk = lane >> 4;
@@ -334,8 +405,14 @@ __global__ __launch_bounds__(512) void k2_contract_ppp(const bf16* __restrict__ 
 
     int kin = 0;                                        // step within the current tile
     int tl = 0;
-    int rsl = 0;                                        // ring slot of step s
-    for (int s = 0; s < S; ++s) {
+    int nk_cur;                                         // steps of tile tl
+    {
+        size_t bc; int ti, tj, klo; bool lv;
+        tile_geo(0, bc, ti, tj);
+        krange(bc, ti, tj, klo, nk_cur, lv);
+    }
+    int rsl = 0;                                        // ring slot of the current step
+    for (;;) {
         // M_s
         const unsigned char* st = smem + rsl * STB;
         if (++rsl == NSP) rsl = 0;
@@ -354,11 +431,12 @@ __global__ __launch_bounds__(512) void k2_contract_ppp(const bf16* __restrict__ 
             for (int n = 0; n < 4; ++n) acc[m][n] = Elem<bf16>::mma(fb[n], fa[m], acc[m][n]);
         __builtin_amdgcn_s_waitcnt(waitcnt_vm((DIST - 1) * DPS));
         barrier();
-        if (++kin == nk) {
+        if (++kin == nk_cur) {
             // Tile tl complete: store this wave's block and start the next.
-            size_t bc; int i0, j0;
-            tile_geo(tl, bc, i0, j0);
-            bf16* Ob = O + bc * slab;
+            size_t bc; int ti, tj;
+            tile_geo(tl, bc, ti, tj);
+            const int i0 = ti * BM, j0 = tj * BN;
+            bf16* Ob = args.O + bc * args.o_stride;
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
                 const int i = i0 + wm * 128 + m * 16 + (lane & 15);
@@ -378,26 +456,195 @@ __global__ __launch_bounds__(512) void k2_contract_ppp(const bf16* __restrict__ 
                 }
             }
             kin = 0;
-            ++tl;
+            if (++tl == n_my) break;
+            size_t nbc; int nti, ntj, klo; bool lv;
+            tile_geo(tl, nbc, nti, ntj);
+            krange(nbc, nti, ntj, klo, nk_cur, lv);
         }
     }
     if (wm == 0) barrier();                             // balance group 1's extra barrier
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));          // no DMA may outlive the workgroup
 }
 
-template <typename T, int BM, int BN>
-static hipError_t launch_k2(const void* a, const void* b, int B, int C, int N, void* o,
-                            hipStream_t s)
+// ---------------------------------------------------------------------------
+// Live key ranges of the contraction's row tiles, read from the pair mask.
+//
+// Row r, key k of both operands is scaled by M[r][k] = mask[b][r][k]
+// (outgoing) or mask[b][k][r] (incoming), so where M is zero for every row of
+// a row tile, every product of that tile with that key is an exact zero.
+// ranges[b][t] = (lo, hi) in K-steps of 32 keys: every key outside
+// [32 lo, 32 hi) is zero for all rows of tile t; (0, 0) if no key is live.
+// A mask value counts as live unless it compares equal to zero (-0 is zero,
+// NaN is live, so a NaN still reaches the output).
+// One 256-thread workgroup per (tile, batch element) reads the tile's mask
+// rows (outgoing) or columns (incoming) once, in 16-byte chunks.
+// ---------------------------------------------------------------------------
+template <typename T>
+__device__ inline bool mask_live(T v) { return v != (T)0; }
+
+template <typename T>
+__global__ __launch_bounds__(256) void k0_mask_ranges(const T* __restrict__ mask, int N, int incoming,
+                                                      int* __restrict__ ranges, int* __restrict__ hdr)
 {
-    const int tiles_i = (N + BM - 1) / BM, tiles_j = (N + BN - 1) / BN;
-    dim3 grid((unsigned)((size_t)tiles_i * tiles_j * B * C));
-    hipLaunchKernelGGL((k2_contract<T, BM, BN>), grid, dim3(256), 0, s,
-                       (const T*)a, (const T*)b, (T*)o, N, tiles_j);
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 4) hdr[threadIdx.x] = 0;
+    constexpr int CE = 16 / (int)sizeof(T);        // elements per 16-byte chunk
+    const int t = blockIdx.x, b = blockIdx.y, tiles = gridDim.x;
+    const int tid = threadIdx.x;
+    const T* m = mask + (size_t)b * N * N;
+    const int r0 = t * K2_TILE, rows = min(N, r0 + K2_TILE) - r0;   // multiple of 8
+    int kmin = 0x7fffffff, kmax = -1;
+    if (!incoming) {
+        // Rows r0 .. r0 + rows - 1 of the mask, keys along the row.
+        const int nch = N / CE;
+        for (int r = 0; r < rows; ++r) {
+            const T* row = m + (size_t)(r0 + r) * N;
+            for (int c = tid; c < nch; c += 256) {
+                const u32x4 v = ld16(row + (size_t)c * CE);
+                const T* e = reinterpret_cast<const T*>(&v);
+#pragma unroll
+                for (int q = 0; q < CE; ++q)
+                    if (mask_live(e[q])) {
+                        kmin = min(kmin, c * CE + q);
+                        kmax = max(kmax, c * CE + q);
+                    }
+            }
+        }
+    } else {
+        // Columns r0 .. r0 + rows - 1 of every mask row k: key k is live if any
+        // of them is.
+        const int cpr = rows / CE;                  // chunks per mask row (1 .. 64)
+        const int rpi = 256 / cpr;                  // mask rows per pass
+        const int c = tid % cpr, k0 = tid / cpr;
+        if (k0 < rpi)
+            for (int k = k0; k < N; k += rpi) {
+                const u32x4 v = ld16(m + (size_t)k * N + r0 + c * CE);
+                const T* e = reinterpret_cast<const T*>(&v);
+                bool live = false;
+#pragma unroll
+                for (int q = 0; q < CE; ++q) live |= mask_live(e[q]);
+                if (live) {
+                    kmin = min(kmin, k);
+                    kmax = max(kmax, k);
+                }
+            }
+    }
+    // Workgroup min / max.
+    for (int off = 32; off > 0; off >>= 1) {
+        kmin = min(kmin, __shfl_xor(kmin, off));
+        kmax = max(kmax, __shfl_xor(kmax, off));
+    }
+    __shared__ int smin[4], smax[4];
+    if ((tid & 63) == 0) { smin[tid >> 6] = kmin; smax[tid >> 6] = kmax; }
+    __syncthreads();
+    if (tid == 0) {
+        kmin = min(min(smin[0], smin[1]), min(smin[2], smin[3]));
+        kmax = max(max(smax[0], smax[1]), max(smax[2], smax[3]));
+        int* dst = ranges + ((size_t)b * tiles + t) * 2;
+        dst[0] = kmax < 0 ? 0 : kmin / K2_KSTEP;
+        dst[1] = kmax < 0 ? 0 : kmax / K2_KSTEP + 1;
+    }
+}
+
+hipError_t launch_mask_ranges(const Params& p, const void* mask, int B, int N, int incoming, int* table,
+                              hipStream_t s)
+{
+    const int tiles = (N + K2_TILE - 1) / K2_TILE;
+    int* hdr = table + 2 * (size_t)B * tiles;
+    dim3 grid((unsigned)tiles, (unsigned)B);
+    if (p.dtype == DType::BF16)
+        hipLaunchKernelGGL(k0_mask_ranges<bf16>, grid, dim3(256), 0, s, (const bf16*)mask, N, incoming, table, hdr);
+    else
+        hipLaunchKernelGGL(k0_mask_ranges<float>, grid, dim3(256), 0, s, (const float*)mask, N, incoming, table,
+                           hdr);
     return hipGetLastError();
 }
 
-hipError_t launch_contract(const Params& p, const void* a_cm, const void* b_cm, int B, int N,
-                           void* o, hipStream_t s)
+// Each batch's tile pairs, walked as the contraction walks a channel (groups
+// of gm row tiles, column by column), split stably into pairs with at least
+// one live K-step and the rest; the header gets the largest live count over
+// the batches (its clear is done by the range scan, which runs first).  One
+// workgroup per batch element; two passes over the T^2 <= 16384 pairs.
+__global__ __launch_bounds__(256) void k0_tile_pairs(int* __restrict__ table, int B, int T, int gm)
+{
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int* rg = table + (size_t)b * T * 2;
+    int* hdr = table + 2 * (size_t)B * T;
+    unsigned* pairs = reinterpret_cast<unsigned*>(hdr + 4) + (size_t)b * T * T;
+    const int T2 = T * T;
+    auto pair_at = [&](int q, int& ti, int& tj) {
+        const int first_i = (q / (gm * T)) * gm;
+        const int g = min(gm, T - first_i);
+        ti = first_i + (q % (gm * T)) % g;
+        tj = (q % (gm * T)) / g;
+    };
+    auto live_at = [&](int ti, int tj) {
+        return max(rg[2 * ti], rg[2 * tj]) < min(rg[2 * ti + 1], rg[2 * tj + 1]);
+    };
+    __shared__ int wl[4], wd[4];
+    int cnt = 0;
+    for (int q = tid; q < T2; q += 256) {
+        int ti, tj;
+        pair_at(q, ti, tj);
+        cnt += live_at(ti, tj) ? 1 : 0;
+    }
+    for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off);
+    if (lane == 0) wl[wave] = cnt;
+    __syncthreads();
+    const int nlive = wl[0] + wl[1] + wl[2] + wl[3];
+    __syncthreads();
+    int base_l = 0, base_d = nlive;
+    const unsigned long long below = (1ull << lane) - 1ull;
+    for (int q0 = 0; q0 < T2; q0 += 256) {
+        const int q = q0 + tid;
+        int ti = 0, tj = 0;
+        bool live = false;
+        if (q < T2) {
+            pair_at(q, ti, tj);
+            live = live_at(ti, tj);
+        }
+        const unsigned long long bl = __ballot(q < T2 && live), bd = __ballot(q < T2 && !live);
+        if (lane == 0) {
+            wl[wave] = __popcll(bl);
+            wd[wave] = __popcll(bd);
+        }
+        __syncthreads();
+        int ol = 0, od = 0, tl = 0, td = 0;
+        for (int w = 0; w < 4; ++w) {
+            if (w < wave) { ol += wl[w]; od += wd[w]; }
+            tl += wl[w];
+            td += wd[w];
+        }
+        if (q < T2) {
+            const unsigned e = (unsigned)ti | ((unsigned)tj << 16);
+            if (live) pairs[base_l + ol + __popcll(bl & below)] = e;
+            else pairs[base_d + od + __popcll(bd & below)] = e;
+        }
+        base_l += tl;
+        base_d += td;
+        __syncthreads();
+    }
+    if (tid == 0) atomicMax(hdr, nlive);
+}
+
+hipError_t launch_tile_pairs(const Plan& plan, int* table, int B, int N, hipStream_t s)
+{
+    const int tiles = (N + K2_TILE - 1) / K2_TILE;
+    hipLaunchKernelGGL(k0_tile_pairs, dim3((unsigned)B), dim3(256), 0, s, table, B, tiles, plan.k2_gm);
+    return hipGetLastError();
+}
+
+template <typename T, int BM, int BN>
+static hipError_t launch_k2(const void* a, const void* b, int N, const ContractJob& job, hipStream_t s)
+{
+    const int tiles_i = (N + BM - 1) / BM, tiles_j = (N + BN - 1) / BN;
+    dim3 grid((unsigned)((size_t)tiles_i * tiles_j * job.nbc));
+    hipLaunchKernelGGL((k2_contract<T, BM, BN>), grid, dim3(256), 0, s,
+                       (const T*)a, (const T*)b, (T*)job.o, job.o_stride, job.bc0, N, tiles_j);
+    return hipGetLastError();
+}
+
+hipError_t launch_contract(const Params& p, const Plan& plan, const void* a_cm, const void* b_cm,
+                           int B, int N, const ContractJob& job, hipStream_t s)
 {
     // bf16: the persistent 256 x 256 kernel at every N (measured faster than
     // 128 x 128 tiles down to N = 384 as well: 0.031 against 0.036 ms for
@@ -405,16 +652,31 @@ hipError_t launch_contract(const Params& p, const void* a_cm, const void* b_cm, 
     // never stored.
     if (p.dtype == DType::BF16) {
         const int tiles = (N + k2big::BM - 1) / k2big::BM;
-        const long long total = (long long)tiles * tiles * B * p.C;
+        const long long total = (long long)tiles * tiles * job.nbc;   // a multiple of 8: 8 | nbc
         int dev = 0, cus = 256;
         if (hipGetDevice(&dev) == hipSuccess)
             (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        cus &= ~7;                                                      // G a multiple of 8
         const long long pg = total < cus ? total : cus;
-        hipLaunchKernelGGL(k2_contract_ppp<4>, dim3((unsigned)pg), dim3(512), 0, s, (const bf16*)a_cm,
-                           (const bf16*)b_cm, (bf16*)o, N, (int)total);
+        K2PArgs a;
+        a.A = (const bf16*)a_cm;
+        a.Bm = (const bf16*)b_cm;
+        a.O = (bf16*)job.o;
+        a.o_stride = job.o_stride;
+        const int T = (N + K2_TILE - 1) / K2_TILE;
+        a.ranges = job.table;
+        a.hdr = job.table ? job.table + 2 * (size_t)B * T : nullptr;
+        a.pairs = job.table ? reinterpret_cast<const unsigned*>(job.table + 2 * (size_t)B * T + 4) : nullptr;
+        a.N = N;
+        a.C = p.C;
+        a.total = (int)total;
+        a.bc0 = job.bc0;
+        a.order = plan.k2_order;
+        a.gm = plan.k2_gm;
+        hipLaunchKernelGGL(k2_contract_ppp<4>, dim3((unsigned)pg), dim3(512), 0, s, a);
         return hipGetLastError();
     }
-    return launch_k2<float, 128, 128>(a_cm, b_cm, B, p.C, N, o, s);
+    return launch_k2<float, 128, 128>(a_cm, b_cm, N, job, s);
 }
 
 }  // namespace trimul

@@ -34,9 +34,19 @@ struct K3Cfg {
     static constexpr int OCH = TM / CE;                   // chunks per o-tile row
 };
 
+// Slab bc of o under an OutputSrc: the first `split` slabs are contiguous at
+// o_lo; the rest sit at o_hi with their own stride (the workspace-lean layout
+// puts them over operand slabs the contraction has finished with).
+template <typename T>
+__device__ inline const T* o_slab(const OutputSrc& os, size_t bc, size_t NN)
+{
+    return bc < (size_t)os.split ? (const T*)os.o_lo + bc * NN
+                                 : (const T*)os.o_hi + (bc - (size_t)os.split) * os.hi_stride;
+}
+
 template <typename T, int D, int C>
 __global__ __launch_bounds__(256) void k3_output(
-    const T* __restrict__ z, const T* __restrict__ o, const T* __restrict__ Wgo,
+    const T* __restrict__ z, const OutputSrc osrc, const T* __restrict__ Wgo,
     const T* __restrict__ Wpo, const float* __restrict__ lnw_in, const float* __restrict__ lnb_in,
     const float* __restrict__ lnw_out, const float* __restrict__ lnb_out, float eps,
     T* __restrict__ out, int N, int blocks_per_b)
@@ -62,11 +72,11 @@ __global__ __launch_bounds__(256) void k3_output(
     // Stage o[:, p0 : p0+TM] into LDS as otile[c][pair].
     const u32x4 zero = {0u, 0u, 0u, 0u};
     {
-        const T* ob = o + (size_t)bidx * C * NN + p0;
         u32x4* ot = reinterpret_cast<u32x4*>(otile);
         for (int idx = tid; idx < C * OCH; idx += 256) {
             const int c = idx / OCH, ch = idx % OCH;
-            ot[idx] = (ch * CE < tvalid) ? ld16(ob + (size_t)c * NN + ch * CE) : zero;
+            const T* oc = o_slab<T>(osrc, (size_t)bidx * C + c, NN);
+            ot[idx] = (ch * CE < tvalid) ? ld16(oc + p0 + ch * CE) : zero;
         }
     }
 
@@ -306,7 +316,7 @@ template <> struct OFrags<4> {
 
 template <int D, int C>
 __global__ __launch_bounds__(k3f::waves_for(D) * 64) void k3_output_fold(
-    const bf16* __restrict__ z, const bf16* __restrict__ o, const bf16* __restrict__ Wg,
+    const bf16* __restrict__ z, const OutputSrc osrc, const bf16* __restrict__ Wg,
     const bf16* __restrict__ Wp, const bf16* __restrict__ Xg, const bf16* __restrict__ Xp,
     float eps, bf16* __restrict__ out, int N, int n_super)
 {
@@ -370,7 +380,7 @@ __global__ __launch_bounds__(k3f::waves_for(D) * 64) void k3_output_fold(
                 const int qo = q - Cf::ZDMA;
                 const int c = qo * 16 + (ln >> 2), pc = ln & 3;
                 const int half = (pc >> 1) ^ ((c >> 3) & 1);
-                const bf16* src = o + (bidx * C + c) * NN + pin + half * 16 + (pc & 1) * 8;
+                const bf16* src = o_slab<bf16>(osrc, bidx * C + c, NN) + pin + half * 16 + (pc & 1) * 8;
                 dma16_to_lds(src, sl + (uint32_t)(ZB + qo * 1024));
             }
         }
@@ -527,14 +537,14 @@ __global__ __launch_bounds__(k3f::waves_for(D) * 64) void k3_output_fold(
 }
 
 template <typename T, int D, int C>
-static hipError_t launch_k3_t(const Params& p, const void* z, const void* o, int B, int N,
+static hipError_t launch_k3_t(const Params& p, const void* z, const OutputSrc& o, int B, int N,
                               void* out, hipStream_t s)
 {
     using Cf = K3Cfg<T, D, C>;
     const size_t NN = (size_t)N * N;
     const int blocks_per_b = (int)((NN + Cf::TM - 1) / Cf::TM);
     dim3 grid((unsigned)((size_t)B * blocks_per_b));
-    hipLaunchKernelGGL((k3_output<T, D, C>), grid, dim3(256), 0, s, (const T*)z, (const T*)o,
+    hipLaunchKernelGGL((k3_output<T, D, C>), grid, dim3(256), 0, s, (const T*)z, o,
                        (const T*)p.w_gout, (const T*)p.w_pout, p.ln_in_w, p.ln_in_b, p.ln_out_w,
                        p.ln_out_b, p.eps, (T*)out, N, blocks_per_b);
     return hipGetLastError();
@@ -554,7 +564,7 @@ static hipError_t launch_k3_t(const Params& p, const void* z, const void* o, int
     }
 
 template <int D, int C>
-static hipError_t launch_k3_fold(const Params& p, const void* z, const void* o, int B, int N,
+static hipError_t launch_k3_fold(const Params& p, const void* z, const OutputSrc& o, int B, int N,
                                  void* out, hipStream_t s)
 {
     const long long n_super = (long long)B * N * N / 64;   // N % 8 == 0, so N*N % 64 == 0
@@ -565,14 +575,14 @@ static hipError_t launch_k3_fold(const Params& p, const void* z, const void* o, 
     const long long slots = (long long)cus * (8 / NW);       // workgroups resident at once
     const long long grid = n_super < slots ? n_super : slots;
     hipLaunchKernelGGL((k3_output_fold<D, C>), dim3((unsigned)grid), dim3(NW * 64), 0, s, (const bf16*)z,
-                       (const bf16*)o, (const bf16*)p.w_gout_f, (const bf16*)p.w_pout_f,
+                       o, (const bf16*)p.w_gout_f, (const bf16*)p.w_pout_f,
                        (const bf16*)p.x_gout, (const bf16*)p.x_pout, p.eps, (bf16*)out, N,
                        (int)n_super);
     return hipGetLastError();
 }
 
 template <typename T>
-static hipError_t launch_k3_d(const Params& p, const void* z, const void* o, int B, int N,
+static hipError_t launch_k3_d(const Params& p, const void* z, const OutputSrc& o, int B, int N,
                               void* out, hipStream_t s)
 {
     switch (p.D) {
@@ -593,7 +603,7 @@ bool output_supported(int D, int C, DType)
     return D >= 32 && D <= 256 && D % 32 == 0 && C >= 32 && C <= 256 && C % 32 == 0;
 }
 
-hipError_t launch_output(const Params& p, const void* z, const void* o, int B, int N, void* out,
+hipError_t launch_output(const Params& p, const void* z, const OutputSrc& o, int B, int N, void* out,
                          hipStream_t s)
 {
     if (p.dtype == DType::BF16 && p.D == 256 && p.C == 256)

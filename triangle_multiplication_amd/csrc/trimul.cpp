@@ -13,17 +13,23 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <algorithm>
+#include <mutex>
 #include <string>
 #include <vector>
 
 #include "trimul.h"
 #include "trimul_internal.h"
 #include "trimul_launch.hpp"
+#include "trimul_plans.hpp"
 
 struct trimul_handle {
     trimul::Params p;
     void* dev_mem;
     int device;
+    std::string arch;                   // device architecture name (cache key)
+    std::mutex mu;                      // guards plans
+    std::vector<trimul::PlanEntry> plans;
 };
 
 namespace {
@@ -143,6 +149,204 @@ trimul_status check_handle_device(const trimul_handle* h)
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+int device_cus()
+{
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess)
+        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    return cus;
+}
+
+// Workspace carving.  Full layout: a | b | o | mask table.  Lean layout: a | b |
+// spare | mask table, where the contraction runs in chunks of `chunk` slabs: the
+// first chunk's o goes to the spare region, chunk t's o over the a slabs of
+// chunk t - 1 (which chunk t - 1 has finished reading; stream order), so o
+// needs only one chunk of memory of its own.  chunk is the smallest multiple
+// of 8 slabs that gives every workgroup of a persistent launch at least 8
+// tiles (8 * 256 tiles), at most all B*C slabs.
+struct WsLayout {
+    size_t a, b, o, ranges, total;   // byte offsets and size
+    int chunk;                       // slabs per contraction launch (B*C when not lean)
+    bool lean;
+};
+
+WsLayout ws_layout(int C, trimul_dtype dt, int B, int N, bool lean)
+{
+    const trimul::DType t = dt == TRIMUL_BF16 ? trimul::DType::BF16 : trimul::DType::FP32;
+    const size_t es = elem_size(dt), NN = (size_t)N * N;
+    const int nbc = B * C;
+    WsLayout L;
+    L.lean = lean;
+    L.chunk = nbc;
+    if (lean) {
+        const long long tiles = (N + trimul::K2_TILE - 1) / trimul::K2_TILE;
+        const long long want = 8LL * 256;
+        long long ch = 8;
+        while (ch < nbc && ch * tiles * tiles < want) ch += 8;
+        L.chunk = (int)(ch < nbc ? ch : nbc);
+    }
+    const size_t ab = align256((size_t)nbc * trimul::ab_slab_elems(t, N) * es);
+    const size_t ob = align256((size_t)L.chunk * NN * es);
+    const size_t rb = align256(trimul::mask_table_ints(B, N) * sizeof(int));
+    L.a = 0;
+    L.b = ab;
+    L.o = 2 * ab;
+    L.ranges = L.o + ob;
+    L.total = L.ranges + rb;
+    return L;
+}
+
+// One validated forward call.
+struct FwdCall {
+    const void* z;
+    const void* mask;
+    int B, N, incoming;
+    void* out;
+    uint8_t* ws;
+    WsLayout L;
+};
+
+trimul::PlanKey key_of(const FwdCall& c) { return {c.B, c.N, c.incoming, c.mask ? 1 : 0}; }
+
+trimul::Plan plan_lookup(trimul_handle* h, const trimul::PlanKey& k)
+{
+    std::lock_guard<std::mutex> g(h->mu);
+    for (const trimul::PlanEntry& e : h->plans)
+        if (e.key == k) return e.plan;
+    return trimul::Plan{};
+}
+
+trimul::Plan plan_for(trimul_handle* h, const FwdCall& c) { return plan_lookup(h, key_of(c)); }
+
+void set_plan(trimul_handle* h, const trimul::PlanEntry& ent)
+{
+    std::lock_guard<std::mutex> g(h->mu);
+    for (trimul::PlanEntry& e : h->plans)
+        if (e.key == ent.key) {
+            e = ent;
+            return;
+        }
+    h->plans.push_back(ent);
+}
+
+// Every check of trimul_fwd, before anything is enqueued.  The workspace
+// layout is the full one when the workspace holds it, else the lean one.
+trimul_status prepare_fwd(trimul_handle* h, const void* z, const void* pair_mask, int B, int N,
+                          trimul_direction dir, void* out, void* workspace, size_t workspace_bytes,
+                          FwdCall& c)
+{
+    if (!h) return fail(TRIMUL_ERR_INVALID_ARG, "handle is NULL");
+    if (!z) return fail(TRIMUL_ERR_INVALID_ARG, "z is NULL");
+    if (!out) return fail(TRIMUL_ERR_INVALID_ARG, "out is NULL");
+    if (dir != TRIMUL_OUTGOING && dir != TRIMUL_INCOMING)
+        return fail(TRIMUL_ERR_INVALID_ARG, "direction must be TRIMUL_OUTGOING or TRIMUL_INCOMING; got %d", (int)dir);
+    trimul_status st = check_shape(h, B, N);
+    if (st != TRIMUL_OK) return st;
+    const trimul_dtype dt = (trimul_dtype)h->p.dtype;
+    const size_t es = elem_size(dt);
+    if (!aligned(z, 16)) return fail(TRIMUL_ERR_INVALID_ARG, "z must be 16-byte aligned");
+    if (!aligned(out, 16)) return fail(TRIMUL_ERR_INVALID_ARG, "out must be 16-byte aligned");
+    if (pair_mask && !aligned(pair_mask, 16)) return fail(TRIMUL_ERR_INVALID_ARG, "pair_mask must be 16-byte aligned");
+    const WsLayout full = ws_layout(h->p.C, dt, B, N, false);
+    const WsLayout lean = ws_layout(h->p.C, dt, B, N, true);
+    if (!workspace)
+        return fail(TRIMUL_ERR_WORKSPACE, "workspace is NULL (%zu bytes required, %zu with the lean layout)",
+                    full.total, lean.total);
+    if (workspace_bytes < lean.total)
+        return fail(TRIMUL_ERR_WORKSPACE,
+                    "workspace of %zu bytes is smaller than the %zu required (%zu with the lean layout)",
+                    workspace_bytes, full.total, lean.total);
+    if (!aligned(workspace, 256)) return fail(TRIMUL_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    c.L = workspace_bytes >= full.total ? full : lean;
+    const size_t need = c.L.total;
+    const size_t NN = (size_t)N * N;
+    const size_t zbytes = (size_t)B * NN * h->p.D * es;
+    const size_t mbytes = pair_mask ? (size_t)B * NN * es : 0;
+    if (overlaps(out, zbytes, z, zbytes)) return fail(TRIMUL_ERR_INVALID_ARG, "out overlaps z");
+    if (overlaps(out, zbytes, pair_mask, mbytes)) return fail(TRIMUL_ERR_INVALID_ARG, "out overlaps pair_mask");
+    if (overlaps(out, zbytes, workspace, need)) return fail(TRIMUL_ERR_INVALID_ARG, "out overlaps the workspace");
+    if (overlaps(z, zbytes, workspace, need)) return fail(TRIMUL_ERR_INVALID_ARG, "z overlaps the workspace");
+    if (overlaps(pair_mask, mbytes, workspace, need))
+        return fail(TRIMUL_ERR_INVALID_ARG, "pair_mask overlaps the workspace");
+    st = check_handle_device(h);
+    if (st != TRIMUL_OK) return st;
+    c.z = z;
+    c.mask = pair_mask;
+    c.B = B;
+    c.N = N;
+    c.incoming = dir == TRIMUL_INCOMING;
+    c.out = out;
+    c.ws = static_cast<uint8_t*>(workspace);
+    return TRIMUL_OK;
+}
+
+bool uses_ranges(const trimul_handle* h, const FwdCall& c)
+{
+    return c.mask && h->p.dtype == trimul::DType::BF16;
+}
+
+// The mask scan (masked bf16 calls) and the projection.
+hipError_t enq_project(const trimul_handle* h, const FwdCall& c, hipStream_t s)
+{
+    hipError_t e = hipSuccess;
+    if (uses_ranges(h, c))
+        e = trimul::launch_mask_ranges(h->p, c.mask, c.B, c.N, c.incoming, (int*)(c.ws + c.L.ranges), s);
+    if (e == hipSuccess)
+        e = trimul::launch_project(h->p, c.z, c.mask, c.B, c.N, c.incoming, c.ws + c.L.a, c.ws + c.L.b, s);
+    return e;
+}
+
+size_t ab_slab_bytes(const trimul_handle* h, int N)
+{
+    return trimul::ab_slab_elems(h->p.dtype, N) * elem_size((trimul_dtype)h->p.dtype);
+}
+
+// The contraction (after the pair lists of a masked call), in one launch or
+// (lean layout) one launch per chunk.
+hipError_t enq_contract(const trimul_handle* h, const trimul::Plan& plan, const FwdCall& c, hipStream_t s)
+{
+    const int nbc = c.B * h->p.C;
+    const size_t es = elem_size((trimul_dtype)h->p.dtype), slab = ab_slab_bytes(h, c.N);
+    int* table = uses_ranges(h, c) ? (int*)(c.ws + c.L.ranges) : nullptr;
+    hipError_t e = table ? trimul::launch_tile_pairs(plan, table, c.B, c.N, s) : hipSuccess;
+    for (int bc0 = 0; bc0 < nbc && e == hipSuccess; bc0 += c.L.chunk) {
+        trimul::ContractJob job;
+        job.bc0 = bc0;
+        job.nbc = std::min(c.L.chunk, nbc - bc0);
+        if (bc0 == 0) {
+            job.o = c.ws + c.L.o;
+            job.o_stride = (size_t)c.N * c.N;
+        } else {
+            job.o = c.ws + c.L.a + (size_t)(bc0 - c.L.chunk) * slab;
+            job.o_stride = slab / es;
+        }
+        job.table = table;
+        e = trimul::launch_contract(h->p, plan, c.ws + c.L.a, c.ws + c.L.b, c.B, c.N, job, s);
+    }
+    return e;
+}
+
+hipError_t enq_output(const trimul_handle* h, const FwdCall& c, hipStream_t s)
+{
+    trimul::OutputSrc os;
+    os.o_lo = c.ws + c.L.o;
+    os.o_hi = c.ws + c.L.a;
+    os.split = c.L.chunk;
+    os.hi_stride = ab_slab_bytes(h, c.N) / elem_size((trimul_dtype)h->p.dtype);
+    return trimul::launch_output(h->p, c.z, os, c.B, c.N, c.out, s);
+}
+
+trimul_status enqueue_fwd(const trimul_handle* h, const trimul::Plan& plan, const FwdCall& c, hipStream_t s)
+{
+    hipError_t e = enq_project(h, c, s);
+    if (e != hipSuccess) return hip_fail("projection kernel launch", e);
+    e = enq_contract(h, plan, c, s);
+    if (e != hipSuccess) return hip_fail("contraction kernel launch", e);
+    e = enq_output(h, c, s);
+    if (e != hipSuccess) return hip_fail("output kernel launch", e);
+    return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -177,10 +381,7 @@ trimul_status trimul_workspace_query(int D, int C, trimul_dtype dtype, int B, in
     if (!width_ok(D) || !width_ok(C))
         return fail(TRIMUL_ERR_UNSUPPORTED, "D and C must be multiples of 32 in [32, 256]; got D=%d C=%d", D, C);
     if (B < 1 || N < 1) return fail(TRIMUL_ERR_INVALID_ARG, "B and N must be >= 1; got B=%d N=%d", B, N);
-    const trimul::DType t = dtype == TRIMUL_BF16 ? trimul::DType::BF16 : trimul::DType::FP32;
-    const size_t ab = align256((size_t)B * C * trimul::ab_slab_elems(t, N) * elem_size(dtype));
-    const size_t o = align256((size_t)B * C * (size_t)N * N * elem_size(dtype));
-    *bytes = 2 * ab + o;
+    *bytes = ws_layout(C, dtype, B, N, false).total;
     return ok();
 }
 
@@ -188,6 +389,15 @@ trimul_status trimul_workspace_size(const trimul_handle* h, int B, int N, size_t
 {
     if (!h) return fail(TRIMUL_ERR_INVALID_ARG, "handle is NULL");
     return trimul_workspace_query(h->p.D, h->p.C, (trimul_dtype)h->p.dtype, B, N, bytes);
+}
+
+trimul_status trimul_workspace_size_lean(const trimul_handle* h, int B, int N, size_t* bytes)
+{
+    if (!h) return fail(TRIMUL_ERR_INVALID_ARG, "handle is NULL");
+    if (!bytes) return fail(TRIMUL_ERR_INVALID_ARG, "bytes is NULL");
+    if (B < 1 || N < 1) return fail(TRIMUL_ERR_INVALID_ARG, "B and N must be >= 1; got B=%d N=%d", B, N);
+    *bytes = ws_layout(h->p.C, (trimul_dtype)h->p.dtype, B, N, true).total;
+    return ok();
 }
 
 trimul_status trimul_create(int D, int C, trimul_dtype dtype, const trimul_weights* w,
@@ -309,6 +519,10 @@ trimul_status trimul_create(int D, int C, trimul_dtype dtype, const trimul_weigh
     h->p.w_proj_f = folded ? base + off_wpf : nullptr;
     h->p.x_proj = folded ? base + off_xpj : nullptr;
     h->p.sink = base + off_sink;
+    h->arch = trimul::plan_device_key(prop.gcnArchName, prop.multiProcessorCount);
+    // Plans recorded by trimul_tune in an earlier process (an unreadable cache
+    // only means no recorded plans).
+    (void)trimul::plan_cache_load(trimul::plan_cache_path(), h->arch, D, C, (int)dtype, h->plans);
     *out = h;
     return ok();
 }
@@ -324,51 +538,64 @@ trimul_status trimul_fwd(trimul_handle* h, const void* z, const void* pair_mask,
                          trimul_direction dir, void* out, void* workspace, size_t workspace_bytes,
                          hipStream_t stream)
 {
-    if (!h) return fail(TRIMUL_ERR_INVALID_ARG, "handle is NULL");
-    if (!z) return fail(TRIMUL_ERR_INVALID_ARG, "z is NULL");
-    if (!out) return fail(TRIMUL_ERR_INVALID_ARG, "out is NULL");
-    if (dir != TRIMUL_OUTGOING && dir != TRIMUL_INCOMING)
-        return fail(TRIMUL_ERR_INVALID_ARG, "direction must be TRIMUL_OUTGOING or TRIMUL_INCOMING; got %d", (int)dir);
-    trimul_status st = check_shape(h, B, N);
+    FwdCall c;
+    trimul_status st = prepare_fwd(h, z, pair_mask, B, N, dir, out, workspace, workspace_bytes, c);
     if (st != TRIMUL_OK) return st;
-    const trimul_dtype dt = (trimul_dtype)h->p.dtype;
-    const size_t es = elem_size(dt);
-    if (!aligned(z, 16)) return fail(TRIMUL_ERR_INVALID_ARG, "z must be 16-byte aligned");
-    if (!aligned(out, 16)) return fail(TRIMUL_ERR_INVALID_ARG, "out must be 16-byte aligned");
-    if (pair_mask && !aligned(pair_mask, es))
-        return fail(TRIMUL_ERR_INVALID_ARG, "pair_mask must be aligned to its element size");
-    size_t need = 0;
-    st = trimul_workspace_query(h->p.D, h->p.C, dt, B, N, &need);
-    if (st != TRIMUL_OK) return st;
-    if (!workspace) return fail(TRIMUL_ERR_WORKSPACE, "workspace is NULL (%zu bytes required)", need);
-    if (workspace_bytes < need)
-        return fail(TRIMUL_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required",
-                    workspace_bytes, need);
-    if (!aligned(workspace, 256)) return fail(TRIMUL_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-    const size_t NN = (size_t)N * N;
-    const size_t zbytes = (size_t)B * NN * h->p.D * es;
-    const size_t mbytes = pair_mask ? (size_t)B * NN * es : 0;
-    if (overlaps(out, zbytes, z, zbytes)) return fail(TRIMUL_ERR_INVALID_ARG, "out overlaps z");
-    if (overlaps(out, zbytes, pair_mask, mbytes)) return fail(TRIMUL_ERR_INVALID_ARG, "out overlaps pair_mask");
-    if (overlaps(out, zbytes, workspace, need)) return fail(TRIMUL_ERR_INVALID_ARG, "out overlaps the workspace");
-    if (overlaps(z, zbytes, workspace, need)) return fail(TRIMUL_ERR_INVALID_ARG, "z overlaps the workspace");
-    if (overlaps(pair_mask, mbytes, workspace, need))
-        return fail(TRIMUL_ERR_INVALID_ARG, "pair_mask overlaps the workspace");
-    st = check_handle_device(h);
-    if (st != TRIMUL_OK) return st;
+    return enqueue_fwd(h, plan_for(h, c), c, stream);
+}
 
-    const size_t ab = align256((size_t)B * h->p.C * trimul::ab_slab_elems(h->p.dtype, N) * es);
-    uint8_t* ws = static_cast<uint8_t*>(workspace);
-    void* a = ws;
-    void* b = ws + ab;
-    void* o = ws + 2 * ab;
-    hipError_t e = trimul::launch_project(h->p, z, pair_mask, B, N, dir == TRIMUL_INCOMING, a, b, stream);
-    if (e != hipSuccess) return hip_fail("projection kernel launch", e);
-    e = trimul::launch_contract(h->p, a, b, B, N, o, stream);
-    if (e != hipSuccess) return hip_fail("contraction kernel launch", e);
-    e = trimul::launch_output(h->p, z, o, B, N, out, stream);
-    if (e != hipSuccess) return hip_fail("output kernel launch", e);
-    return ok();
+trimul_status trimul_tune(trimul_handle* h, const void* z, const void* pair_mask, int B, int N,
+                          trimul_direction dir, void* out, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream)
+{
+    FwdCall c;
+    trimul_status st = prepare_fwd(h, z, pair_mask, B, N, dir, out, workspace, workspace_bytes, c);
+    if (st != TRIMUL_OK) return st;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    hipError_t e = hipEventCreate(&e0);
+    if (e == hipSuccess) e = hipEventCreate(&e1);
+    if (e != hipSuccess) {
+        if (e0) (void)hipEventDestroy(e0);
+        return hip_fail("hipEventCreate", e);
+    }
+    // Each candidate: the projection (the lean layout overwrites a while the
+    // contraction runs, so a is rebuilt first), then the contraction timed
+    // between two events; one untimed warm-up, then the best of kReps.
+    constexpr int kReps = 3;
+    const std::vector<trimul::Plan> cands = trimul::candidate_plans();
+    trimul::Plan best = cands[0];
+    double best_ms = 1e300;
+    for (const trimul::Plan& pl : cands) {
+        double t_min = 1e300;
+        for (int r = 0; r <= kReps && e == hipSuccess; ++r) {
+            e = enq_project(h, c, stream);
+            if (e == hipSuccess) e = hipEventRecord(e0, stream);
+            if (e == hipSuccess) e = enq_contract(h, pl, c, stream);
+            if (e == hipSuccess) e = hipEventRecord(e1, stream);
+            if (e == hipSuccess) e = hipEventSynchronize(e1);
+            float ms = 0.f;
+            if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+            if (e == hipSuccess && r > 0 && ms < t_min) t_min = ms;
+        }
+        if (e != hipSuccess) break;
+        if (t_min < best_ms) {
+            best_ms = t_min;
+            best = pl;
+        }
+    }
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    if (e != hipSuccess) return hip_fail("tuning run", e);
+    trimul::PlanEntry ent;
+    ent.key = key_of(c);
+    ent.plan = best;
+    ent.ms = best_ms;
+    set_plan(h, ent);
+    // The cache is best effort: a read-only or missing location only means the
+    // next process tunes again.
+    (void)trimul::plan_cache_store(trimul::plan_cache_path(), h->arch, h->p.D, h->p.C, (int)h->p.dtype, ent);
+    // Leave a correct result in out, computed with the chosen plan.
+    return enqueue_fwd(h, best, c, stream);
 }
 
 trimul_status trimul_internal_project(trimul_handle* h, const void* z, const void* pair_mask, int B,
@@ -383,6 +610,7 @@ trimul_status trimul_internal_project(trimul_handle* h, const void* z, const voi
     if (st != TRIMUL_OK) return st;
     if (!aligned(z, 16) || !aligned(a_cm, 16) || !aligned(b_cm, 16))
         return fail(TRIMUL_ERR_INVALID_ARG, "z, a_cm and b_cm must be 16-byte aligned");
+    if (pair_mask && !aligned(pair_mask, 16)) return fail(TRIMUL_ERR_INVALID_ARG, "pair_mask must be 16-byte aligned");
     st = check_handle_device(h);
     if (st != TRIMUL_OK) return st;
     hipError_t e = trimul::launch_project(h->p, z, pair_mask, B, N, dir == TRIMUL_INCOMING, a_cm, b_cm, stream);
@@ -390,8 +618,26 @@ trimul_status trimul_internal_project(trimul_handle* h, const void* z, const voi
     return ok();
 }
 
-trimul_status trimul_internal_contract(trimul_handle* h, const void* a_cm, const void* b_cm, int B,
-                                       int N, void* o, hipStream_t stream)
+trimul_status trimul_internal_mask_ranges(trimul_handle* h, const void* pair_mask, int B, int N,
+                                          trimul_direction dir, int* table, hipStream_t stream)
+{
+    if (!h) return fail(TRIMUL_ERR_INVALID_ARG, "handle is NULL");
+    if (!pair_mask || !table) return fail(TRIMUL_ERR_INVALID_ARG, "pair_mask and table must be non-NULL");
+    if (dir != TRIMUL_OUTGOING && dir != TRIMUL_INCOMING)
+        return fail(TRIMUL_ERR_INVALID_ARG, "direction must be TRIMUL_OUTGOING or TRIMUL_INCOMING; got %d", (int)dir);
+    trimul_status st = check_shape(h, B, N);
+    if (st != TRIMUL_OK) return st;
+    if (!aligned(pair_mask, 16) || !aligned(table, 16))
+        return fail(TRIMUL_ERR_INVALID_ARG, "pair_mask and table must be 16-byte aligned");
+    st = check_handle_device(h);
+    if (st != TRIMUL_OK) return st;
+    hipError_t e = trimul::launch_mask_ranges(h->p, pair_mask, B, N, dir == TRIMUL_INCOMING, table, stream);
+    if (e != hipSuccess) return hip_fail("mask range kernel launch", e);
+    return ok();
+}
+
+trimul_status trimul_internal_contract(trimul_handle* h, const void* a_cm, const void* b_cm, int* table,
+                                       int B, int N, trimul_direction dir, void* o, hipStream_t stream)
 {
     if (!h) return fail(TRIMUL_ERR_INVALID_ARG, "handle is NULL");
     if (!a_cm || !b_cm || !o) return fail(TRIMUL_ERR_INVALID_ARG, "a_cm, b_cm and o must be non-NULL");
@@ -399,9 +645,22 @@ trimul_status trimul_internal_contract(trimul_handle* h, const void* a_cm, const
     if (st != TRIMUL_OK) return st;
     if (!aligned(a_cm, 16) || !aligned(b_cm, 16) || !aligned(o, 16))
         return fail(TRIMUL_ERR_INVALID_ARG, "a_cm, b_cm and o must be 16-byte aligned");
+    if (dir != TRIMUL_OUTGOING && dir != TRIMUL_INCOMING)
+        return fail(TRIMUL_ERR_INVALID_ARG, "direction must be TRIMUL_OUTGOING or TRIMUL_INCOMING; got %d", (int)dir);
+    if (table && h->p.dtype != trimul::DType::BF16)
+        return fail(TRIMUL_ERR_UNSUPPORTED, "the mask table is used by the bf16 contraction only");
+    if (table && !aligned(table, 16)) return fail(TRIMUL_ERR_INVALID_ARG, "table must be 16-byte aligned");
     st = check_handle_device(h);
     if (st != TRIMUL_OK) return st;
-    hipError_t e = trimul::launch_contract(h->p, a_cm, b_cm, B, N, o, stream);
+    const trimul::Plan plan = plan_lookup(h, {B, N, (int)dir, table ? 1 : 0});
+    trimul::ContractJob job;
+    job.bc0 = 0;
+    job.nbc = B * h->p.C;
+    job.o = o;
+    job.o_stride = (size_t)N * N;
+    job.table = table;
+    hipError_t e = table ? trimul::launch_tile_pairs(plan, table, B, N, stream) : hipSuccess;
+    if (e == hipSuccess) e = trimul::launch_contract(h->p, plan, a_cm, b_cm, B, N, job, stream);
     if (e != hipSuccess) return hip_fail("contraction kernel launch", e);
     return ok();
 }
@@ -417,9 +676,90 @@ trimul_status trimul_internal_output(trimul_handle* h, const void* z, const void
         return fail(TRIMUL_ERR_INVALID_ARG, "z, o and out must be 16-byte aligned");
     st = check_handle_device(h);
     if (st != TRIMUL_OK) return st;
-    hipError_t e = trimul::launch_output(h->p, z, o, B, N, out, stream);
+    trimul::OutputSrc os;
+    os.o_lo = o;
+    os.o_hi = o;
+    os.split = B * h->p.C;
+    os.hi_stride = 0;
+    hipError_t e = trimul::launch_output(h->p, z, os, B, N, out, stream);
     if (e != hipSuccess) return hip_fail("output kernel launch", e);
     return ok();
+}
+
+trimul_status trimul_internal_set_plan(trimul_handle* h, int B, int N, trimul_direction dir, int masked,
+                                       int k2_order, int k2_gm)
+{
+    if (!h) return fail(TRIMUL_ERR_INVALID_ARG, "handle is NULL");
+    trimul::PlanEntry ent;
+    ent.key = {B, N, (int)dir, masked ? 1 : 0};
+    ent.plan.k2_order = k2_order;
+    ent.plan.k2_gm = k2_gm;
+    ent.ms = 0.0;
+    if (!trimul::plan_valid(ent.plan))
+        return fail(TRIMUL_ERR_INVALID_ARG, "no candidate plan has k2_order=%d k2_gm=%d", k2_order, k2_gm);
+    set_plan(h, ent);
+    return ok();
+}
+
+trimul_status trimul_internal_get_plan(trimul_handle* h, int B, int N, trimul_direction dir, int masked,
+                                       int* k2_order, int* k2_gm)
+{
+    if (!h || !k2_order || !k2_gm) return fail(TRIMUL_ERR_INVALID_ARG, "handle and outputs must be non-NULL");
+    const trimul::Plan p = plan_lookup(h, {B, N, (int)dir, masked ? 1 : 0});
+    *k2_order = p.k2_order;
+    *k2_gm = p.k2_gm;
+    return ok();
+}
+
+int trimul_internal_plan_candidates(int* k2_order, int* k2_gm, int cap)
+{
+    const std::vector<trimul::Plan> c = trimul::candidate_plans();
+    for (int i = 0; i < (int)c.size() && i < cap; ++i) {
+        if (k2_order) k2_order[i] = c[i].k2_order;
+        if (k2_gm) k2_gm[i] = c[i].k2_gm;
+    }
+    return (int)c.size();
+}
+
+trimul_status trimul_internal_cache_store(const char* path, const char* device, int D, int C, int dtype,
+                                          int B, int N, int dir, int masked, int k2_order, int k2_gm, double ms)
+{
+    if (!path || !device) return fail(TRIMUL_ERR_INVALID_ARG, "path and device must be non-NULL");
+    trimul::PlanEntry ent;
+    ent.key = {B, N, dir, masked};
+    ent.plan.k2_order = k2_order;
+    ent.plan.k2_gm = k2_gm;
+    ent.ms = ms;
+    if (!trimul::plan_valid(ent.plan))
+        return fail(TRIMUL_ERR_INVALID_ARG, "no candidate plan has k2_order=%d k2_gm=%d", k2_order, k2_gm);
+    if (!trimul::plan_cache_store(path, device, D, C, dtype, ent))
+        return fail(TRIMUL_ERR_INVALID_ARG, "could not write the plan cache %s", path);
+    return ok();
+}
+
+int trimul_internal_cache_lookup(const char* path, const char* device, int D, int C, int dtype, int B, int N,
+                                 int dir, int masked, int* k2_order, int* k2_gm)
+{
+    if (!path || !device) return -1;
+    std::vector<trimul::PlanEntry> v;
+    if (!trimul::plan_cache_load(path, device, D, C, dtype, v)) return -1;
+    const trimul::PlanKey k = {B, N, dir, masked};
+    for (const trimul::PlanEntry& e : v)
+        if (e.key == k) {
+            if (k2_order) *k2_order = e.plan.k2_order;
+            if (k2_gm) *k2_gm = e.plan.k2_gm;
+            return 1;
+        }
+    return 0;
+}
+
+int trimul_internal_cache_path(char* buf, int cap)
+{
+    const std::string p = trimul::plan_cache_path();
+    if (buf && cap > 0) {
+        std::snprintf(buf, (size_t)cap, "%s", p.c_str());
+    }
+    return (int)p.size();
 }
 
 }  // extern "C"

@@ -50,12 +50,70 @@ __host__ __device__ inline size_t ab_slab_elems(DType t, int N)
     return t == DType::BF16 ? n * ((n + 31) & ~(size_t)31) : n * n;
 }
 
+// Kernel variants chosen per shape (by trimul_tune, or the defaults below).
+// None changes what is computed; each only changes the order of the work.
+struct Plan {
+    // Contraction (bf16): which XCD receives which tiles.
+    //  0: the launch's tiles are cut into 8 contiguous bands, one per XCD.
+    //  1: every round of G tiles (one per workgroup) is cut into 8 contiguous
+    //     blocks, so all XCDs work on the same channels at the same time and
+    //     their panel re-reads beyond L2 hit the shared last-level cache.
+    int k2_order = 0;
+    // Row panels per group when a channel's tiles are walked (4, 8 or 16).
+    int k2_gm = 8;
+};
+
+// Tile height of the bf16 contraction; the mask-range table has one entry per
+// row tile of this many rows.
+constexpr int K2_TILE = 256;
+constexpr int K2_KSTEP = 32;
+
+// Table of a masked contraction (int32 units, T = ceil(N / K2_TILE) row tiles):
+//   [0, 2BT)              ranges[b][t] = (lo, hi): K-steps (32 keys) outside
+//                         which every row of row tile t of A and B is zero;
+//   [2BT, 2BT + 4)        header; [0] = most live tile pairs of any batch;
+//   [2BT + 4, + B T^2)    pairs[b][q] = ti | tj << 16: batch b's T^2 tile pairs,
+//                         those with a live step first, each part in the
+//                         plan's walk order.
+inline size_t mask_table_ints(int B, int N)
+{
+    const size_t T = (size_t)((N + K2_TILE - 1) / K2_TILE);
+    return 2 * (size_t)B * T + 4 + (size_t)B * T * T;
+}
+
+// One launch of the contraction: operand slabs [bc0, bc0 + nbc) of the B*C
+// slabs (bc = b * C + c), output of slab bc0 + t at o + t * o_stride elements.
+// table: null, or a mask table whose ranges and pairs are filled (bf16 only).
+struct ContractJob {
+    int bc0, nbc;
+    void* o;
+    size_t o_stride;
+    const int* table;
+};
+
+// Where the output stage reads o: slab bc at o_lo + bc * N * N for bc < split,
+// else at o_hi + (bc - split) * hi_stride elements.
+struct OutputSrc {
+    const void* o_lo;
+    const void* o_hi;
+    int split;
+    size_t hi_stride;
+};
+
 hipError_t launch_project(const Params& p, const void* z, const void* mask, int B, int N,
                           int incoming, void* a_cm, void* b_cm, hipStream_t s);
-hipError_t launch_contract(const Params& p, const void* a_cm, const void* b_cm, int B, int N,
-                           void* o, hipStream_t s);
-hipError_t launch_output(const Params& p, const void* z, const void* o, int B, int N, void* out,
-                         hipStream_t s);
+// Scan the pair mask for each row tile's live key range (the ranges of the
+// mask table; also clears its header).  incoming: rows of A and B are columns
+// of the mask.
+hipError_t launch_mask_ranges(const Params& p, const void* mask, int B, int N, int incoming,
+                              int* table, hipStream_t s);
+// Order each batch's tile pairs live-first in the walk of plan.k2_gm (the
+// pairs and header of the mask table; its ranges must be filled).
+hipError_t launch_tile_pairs(const Plan& plan, int* table, int B, int N, hipStream_t s);
+hipError_t launch_contract(const Params& p, const Plan& plan, const void* a_cm, const void* b_cm,
+                           int B, int N, const ContractJob& job, hipStream_t s);
+hipError_t launch_output(const Params& p, const void* z, const OutputSrc& o, int B, int N,
+                         void* out, hipStream_t s);
 
 // Host mirrors of the kernels' static launch geometry (used for validation).
 bool project_supported(int D, int C, DType t);
