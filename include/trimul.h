@@ -174,6 +174,26 @@ trimul_status trimul_fwd(trimul_handle *h, const void *z, const void *pair_mask,
                          size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * trimul_fwd for callers that cannot allocate (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same kernels and
+ * arguments without the workspace, which comes from a static device array of
+ * TRIMUL_NOALLOC_MAX_BYTES per GPU (loaded with the library, held until the
+ * process ends).  The call allocates nothing and makes no allocating call.
+ * Shapes whose workspace (lean layout when the full one does not fit) exceeds
+ * the array fail with TRIMUL_ERR_UNSUPPORTED before anything is enqueued; at
+ * D = C = 128, B = 1 that allows N up to 416.  Every call on one GPU
+ * uses the same array: calls that overlap in time on one GPU (different
+ * streams, no ordering between them) race and give wrong results; calls
+ * ordered on one stream are safe.  The array's contents are left over from
+ * the previous call, and nothing the kernels read from it needs clearing
+ * (every byte read in a call is written earlier in the same call).  Other
+ * errors as trimul_fwd.
+ */
+#define TRIMUL_NOALLOC_MAX_BYTES (128u << 20)
+trimul_status trimul_fwd_noalloc(trimul_handle *h, const void *z, const void *pair_mask, int B,
+                                 int N, trimul_direction dir, void *out, hipStream_t stream);
+
+/*
  * Tune the kernel plan for this call's shape, then leave the forward result in
  * out.  Blocking: returns after the work on `stream` has finished.
  *

@@ -33,7 +33,7 @@ DIRECTIONS = {"outgoing": TRIMUL_OUTGOING, "incoming": TRIMUL_INCOMING,
               0: TRIMUL_OUTGOING, 1: TRIMUL_INCOMING}
 
 EXPORTED = ["trimul_create", "trimul_destroy", "trimul_workspace_size", "trimul_workspace_query",
-            "trimul_workspace_size_lean", "trimul_fwd", "trimul_tune", "trimul_check_arch",
+            "trimul_workspace_size_lean", "trimul_fwd", "trimul_fwd_noalloc", "trimul_tune", "trimul_check_arch",
             "trimul_status_string", "trimul_last_error",
             "trimul_internal_project", "trimul_internal_mask_ranges", "trimul_internal_contract",
             "trimul_internal_output", "trimul_internal_set_plan", "trimul_internal_get_plan",
@@ -60,6 +60,9 @@ _lib.trimul_workspace_size_lean.argtypes = [_vp, _ci, _ci, ctypes.POINTER(_sz)]
 _lib.trimul_workspace_size_lean.restype = _ci
 _lib.trimul_fwd.argtypes = [_vp, _vp, _vp, _ci, _ci, _ci, _vp, _vp, _sz, _vp]
 _lib.trimul_fwd.restype = _ci
+_lib.trimul_fwd_noalloc.argtypes = [_vp, _vp, _vp, _ci, _ci, _ci, _vp, _vp]
+_lib.trimul_fwd_noalloc.restype = _ci
+NOALLOC_MAX_BYTES = 128 << 20   # TRIMUL_NOALLOC_MAX_BYTES in include/trimul.h
 _lib.trimul_tune.argtypes = [_vp, _vp, _vp, _ci, _ci, _ci, _vp, _vp, _sz, _vp]
 _lib.trimul_tune.restype = _ci
 _lib.trimul_check_arch.argtypes = [ctypes.c_char_p]
@@ -173,6 +176,13 @@ def trimul_fwd(h, z, mask, direction, out, workspace, stream=None):
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(_lib.trimul_fwd(h, _ptr(z), _ptr(mask), B, N, DIRECTIONS.get(direction, direction), _ptr(out),
                            _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def trimul_fwd_noalloc(h, z, mask, direction, out, stream=None):
+    """trimul_fwd with the library's static scratch array as the workspace."""
+    B, N = int(z.shape[0]), int(z.shape[1])
+    _check(_lib.trimul_fwd_noalloc(h, _ptr(z), _ptr(mask), B, N, DIRECTIONS.get(direction, direction),
+                                   _ptr(out), _stream(stream)))
 
 
 def trimul_tune(h, z, mask, direction, out, workspace, stream=None):

@@ -30,7 +30,14 @@ struct trimul_handle {
     std::string arch;                   // device architecture name (cache key)
     std::mutex mu;                      // guards plans
     std::vector<trimul::PlanEntry> plans;
+    void* scratch;                      // this device's address of `scratch` (trimul_fwd_noalloc)
 };
+
+// Workspace of trimul_fwd_noalloc: one array per device, loaded with the
+// library's code object and held until the process ends.  In host code the
+// name is only a stand-in for the symbol; the device address comes from
+// hipGetSymbolAddress, once per device, in trimul_create (scratch_address).
+static __device__ __align__(256) unsigned char scratch[TRIMUL_NOALLOC_MAX_BYTES];
 
 namespace {
 
@@ -134,6 +141,28 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb)
     if (!a || !b || !na || !nb) return false;
     uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
     return x < y + nb && y < x + na;
+}
+
+// Per-device address of `scratch`, looked up once per device with that device
+// current (the caller's), and kept for the life of the process.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices];
+
+trimul_status scratch_address(int dev, void** out)
+{
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(TRIMUL_ERR_UNSUPPORTED, "device ordinal %d is beyond the %d the library tracks", dev, kMaxDevices);
+    std::lock_guard<std::mutex> g(g_scratch_mu);
+    if (!g_scratch_addr[dev]) {
+        void* ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail("hipGetSymbolAddress (scratch)", e);
+        if (!ptr) return fail(TRIMUL_ERR_HIP, "hipGetSymbolAddress (scratch) returned NULL");
+        g_scratch_addr[dev] = ptr;
+    }
+    *out = g_scratch_addr[dev];
+    return TRIMUL_OK;
 }
 
 trimul_status check_handle_device(const trimul_handle* h)
@@ -427,6 +456,9 @@ trimul_status trimul_create(int D, int C, trimul_dtype dtype, const trimul_weigh
     if (e != hipSuccess) return hip_fail("hipGetDeviceProperties", e);
     trimul_status st = trimul_check_arch(prop.gcnArchName);
     if (st != TRIMUL_OK) return st;
+    void* scratch_ptr = nullptr;
+    st = scratch_address(dev, &scratch_ptr);
+    if (st != TRIMUL_OK) return st;
 
     // Host packing.
     const size_t es = elem_size(dtype);
@@ -519,6 +551,7 @@ trimul_status trimul_create(int D, int C, trimul_dtype dtype, const trimul_weigh
     h->p.w_proj_f = folded ? base + off_wpf : nullptr;
     h->p.x_proj = folded ? base + off_xpj : nullptr;
     h->p.sink = base + off_sink;
+    h->scratch = scratch_ptr;
     h->arch = trimul::plan_device_key(prop.gcnArchName, prop.multiProcessorCount);
     // Plans recorded by trimul_tune in an earlier process (an unreadable cache
     // only means no recorded plans).
@@ -540,6 +573,24 @@ trimul_status trimul_fwd(trimul_handle* h, const void* z, const void* pair_mask,
 {
     FwdCall c;
     trimul_status st = prepare_fwd(h, z, pair_mask, B, N, dir, out, workspace, workspace_bytes, c);
+    if (st != TRIMUL_OK) return st;
+    return enqueue_fwd(h, plan_for(h, c), c, stream);
+}
+
+trimul_status trimul_fwd_noalloc(trimul_handle* h, const void* z, const void* pair_mask, int B, int N,
+                                 trimul_direction dir, void* out, hipStream_t stream)
+{
+    if (!h) return fail(TRIMUL_ERR_INVALID_ARG, "handle is NULL");
+    trimul_status st = check_shape(h, B, N);
+    if (st != TRIMUL_OK) return st;
+    const trimul_dtype dt = (trimul_dtype)h->p.dtype;
+    const size_t need = ws_layout(h->p.C, dt, B, N, true).total;
+    if (need > (size_t)TRIMUL_NOALLOC_MAX_BYTES)
+        return fail(TRIMUL_ERR_UNSUPPORTED,
+                    "B=%d N=%d needs %zu bytes of scratch (lean layout); trimul_fwd_noalloc holds %zu: "
+                    "use trimul_fwd with a workspace", B, N, need, (size_t)TRIMUL_NOALLOC_MAX_BYTES);
+    FwdCall c;
+    st = prepare_fwd(h, z, pair_mask, B, N, dir, out, h->scratch, (size_t)TRIMUL_NOALLOC_MAX_BYTES, c);
     if (st != TRIMUL_OK) return st;
     return enqueue_fwd(h, plan_for(h, c), c, stream);
 }
