@@ -52,7 +52,7 @@ def stored_traffic(name, direction, plan):
         return None
     if (t.get("workload") != name or t.get("direction") != direction
             or t.get("sources_sha256") != k2_source_digest()
-            or tuple(t.get("plan", (0, 8))) != tuple(plan)):
+            or tuple(t.get("plan", (0, 0, 8))[1:]) != tuple(plan[1:])):
         return None
     return float(t["hbm_bytes_per_launch"])
 
@@ -344,7 +344,7 @@ def main():
                                "workload or plan differ)" % os.path.relpath(TRAFFIC_FILE, ROOT)),
             "kernel": "k2_contract",
             "per_launch": "2*B*C*N^3 = %.4g FLOP" % k2_flops, "avg_ms": round(k2_ms, 4),
-            "plan": {"k2_order": plan[0], "k2_gm": plan[1]}}
+            "plan": {"k1_variant": plan[0], "k2_order": plan[1], "k2_gm": plan[2]}}
     if use_ranges:
         ex = executed_k2_flops(rng, B, C, N)
         roof["executed_flops_per_launch"] = ex

@@ -97,7 +97,7 @@ def test_tile_pair_lists(tb, gm):
     ms = _masks(N, "bf16")
     mask = torch.cat([ms["tail10"], ms["sparse"], ms["empty"]]).cuda()
     table = layer.mask_ranges(mask, "incoming")
-    tb.trimul_internal_set_plan(layer.h, B, N, "incoming", True, 0, gm)
+    tb.trimul_internal_set_plan(layer.h, B, N, "incoming", True, (0, 0, gm))
     C = 32
     a = torch.zeros(tb.ab_storage_shape("bf16", B, C, N), dtype=torch.bfloat16, device="cuda")
     layer.contract(a, a, table, "incoming")   # builds the lists with the plan's gm
@@ -177,12 +177,12 @@ def test_every_plan_gives_the_same_bits(tb, direction, masked):
     plans = tb.plan_candidates()
     assert tb.trimul_internal_get_plan(layer.h, B, N, direction, masked) == plans[0]
     ref = layer.forward(z, mask, direction)
-    for order, gm in plans[1:]:
-        tb.trimul_internal_set_plan(layer.h, B, N, direction, masked, order, gm)
-        assert tb.trimul_internal_get_plan(layer.h, B, N, direction, masked) == (order, gm)
+    for plan in plans[1:]:
+        tb.trimul_internal_set_plan(layer.h, B, N, direction, masked, plan)
+        assert tb.trimul_internal_get_plan(layer.h, B, N, direction, masked) == plan
         out = layer.forward(z, mask, direction)
         torch.cuda.synchronize()
-        assert torch.equal(out, ref), (order, gm)
+        assert torch.equal(out, ref), plan
     assert oracle_check(z, mask, w, direction, ref, full=False, extra=(N - 1 - N // 10,)) <= 2e-2
 
 
@@ -243,3 +243,4 @@ def test_tune_records_a_plan_and_the_cache_reloads_it(tb, tmp_path):
             os.environ.pop("TRIMUL_PLAN_CACHE", None)
         else:
             os.environ["TRIMUL_PLAN_CACHE"] = old
+

@@ -646,9 +646,10 @@ static hipError_t launch_k1_fold(const Params& p, const void* z, const void* mas
     return hipGetLastError();
 }
 
-hipError_t launch_project(const Params& p, const void* z, const void* mask, int B, int N,
+hipError_t launch_project(const Params& p, const Plan& plan, const void* z, const void* mask, int B, int N,
                           int incoming, void* a_cm, void* b_cm, hipStream_t s)
 {
+    (void)plan;
     if (p.dtype == DType::BF16 && p.D == 256)
         return launch_k1_fold<256>(p, z, mask, B, N, incoming, a_cm, b_cm, s);
     if (p.dtype == DType::BF16 && p.D == 128)

@@ -178,6 +178,21 @@ trimul_status check_handle_device(const trimul_handle* h)
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// The integer a C caller passed for an enum argument.  C allows any int there,
+// while in C++ merely loading an enum object that holds a value outside the
+// enum's range is undefined, so the value is read as its object
+// representation and only validated ints are turned back into enums.
+template <typename E>
+int enum_int(const E* e)
+{
+    static_assert(sizeof(E) == sizeof(int), "C enums are int-sized");
+    int v;
+    std::memcpy(&v, e, sizeof v);
+    return v;
+}
+
+bool direction_ok(int d) { return d == TRIMUL_OUTGOING || d == TRIMUL_INCOMING; }
+
 int device_cus()
 {
     int dev = 0, cus = 256;
@@ -267,8 +282,9 @@ trimul_status prepare_fwd(trimul_handle* h, const void* z, const void* pair_mask
     if (!h) return fail(TRIMUL_ERR_INVALID_ARG, "handle is NULL");
     if (!z) return fail(TRIMUL_ERR_INVALID_ARG, "z is NULL");
     if (!out) return fail(TRIMUL_ERR_INVALID_ARG, "out is NULL");
-    if (dir != TRIMUL_OUTGOING && dir != TRIMUL_INCOMING)
-        return fail(TRIMUL_ERR_INVALID_ARG, "direction must be TRIMUL_OUTGOING or TRIMUL_INCOMING; got %d", (int)dir);
+    const int d = enum_int(&dir);
+    if (!direction_ok(d))
+        return fail(TRIMUL_ERR_INVALID_ARG, "direction must be TRIMUL_OUTGOING or TRIMUL_INCOMING; got %d", d);
     trimul_status st = check_shape(h, B, N);
     if (st != TRIMUL_OK) return st;
     const trimul_dtype dt = (trimul_dtype)h->p.dtype;
@@ -303,7 +319,7 @@ trimul_status prepare_fwd(trimul_handle* h, const void* z, const void* pair_mask
     c.mask = pair_mask;
     c.B = B;
     c.N = N;
-    c.incoming = dir == TRIMUL_INCOMING;
+    c.incoming = d == TRIMUL_INCOMING;
     c.out = out;
     c.ws = static_cast<uint8_t*>(workspace);
     return TRIMUL_OK;
@@ -315,13 +331,13 @@ bool uses_ranges(const trimul_handle* h, const FwdCall& c)
 }
 
 // The mask scan (masked bf16 calls) and the projection.
-hipError_t enq_project(const trimul_handle* h, const FwdCall& c, hipStream_t s)
+hipError_t enq_project(const trimul_handle* h, const trimul::Plan& plan, const FwdCall& c, hipStream_t s)
 {
     hipError_t e = hipSuccess;
     if (uses_ranges(h, c))
         e = trimul::launch_mask_ranges(h->p, c.mask, c.B, c.N, c.incoming, (int*)(c.ws + c.L.ranges), s);
     if (e == hipSuccess)
-        e = trimul::launch_project(h->p, c.z, c.mask, c.B, c.N, c.incoming, c.ws + c.L.a, c.ws + c.L.b, s);
+        e = trimul::launch_project(h->p, plan, c.z, c.mask, c.B, c.N, c.incoming, c.ws + c.L.a, c.ws + c.L.b, s);
     return e;
 }
 
@@ -367,7 +383,7 @@ hipError_t enq_output(const trimul_handle* h, const FwdCall& c, hipStream_t s)
 
 trimul_status enqueue_fwd(const trimul_handle* h, const trimul::Plan& plan, const FwdCall& c, hipStream_t s)
 {
-    hipError_t e = enq_project(h, c, s);
+    hipError_t e = enq_project(h, plan, c, s);
     if (e != hipSuccess) return hip_fail("projection kernel launch", e);
     e = enq_contract(h, plan, c, s);
     if (e != hipSuccess) return hip_fail("contraction kernel launch", e);
@@ -382,7 +398,7 @@ extern "C" {
 
 const char* trimul_status_string(trimul_status s)
 {
-    switch (s) {
+    switch (enum_int(&s)) {
     case TRIMUL_OK: return "TRIMUL_OK";
     case TRIMUL_ERR_INVALID_ARG: return "TRIMUL_ERR_INVALID_ARG";
     case TRIMUL_ERR_UNSUPPORTED: return "TRIMUL_ERR_UNSUPPORTED";
@@ -405,12 +421,13 @@ trimul_status trimul_check_arch(const char* name)
 trimul_status trimul_workspace_query(int D, int C, trimul_dtype dtype, int B, int N, size_t* bytes)
 {
     if (!bytes) return fail(TRIMUL_ERR_INVALID_ARG, "bytes is NULL");
-    if (dtype != TRIMUL_BF16 && dtype != TRIMUL_FP32)
-        return fail(TRIMUL_ERR_INVALID_ARG, "dtype must be TRIMUL_BF16 or TRIMUL_FP32; got %d", (int)dtype);
+    const int dt = enum_int(&dtype);
+    if (dt != TRIMUL_BF16 && dt != TRIMUL_FP32)
+        return fail(TRIMUL_ERR_INVALID_ARG, "dtype must be TRIMUL_BF16 or TRIMUL_FP32; got %d", dt);
     if (!width_ok(D) || !width_ok(C))
         return fail(TRIMUL_ERR_UNSUPPORTED, "D and C must be multiples of 32 in [32, 256]; got D=%d C=%d", D, C);
     if (B < 1 || N < 1) return fail(TRIMUL_ERR_INVALID_ARG, "B and N must be >= 1; got B=%d N=%d", B, N);
-    *bytes = ws_layout(C, dtype, B, N, false).total;
+    *bytes = ws_layout(C, (trimul_dtype)dt, B, N, false).total;
     return ok();
 }
 
@@ -429,14 +446,16 @@ trimul_status trimul_workspace_size_lean(const trimul_handle* h, int B, int N, s
     return ok();
 }
 
-trimul_status trimul_create(int D, int C, trimul_dtype dtype, const trimul_weights* w,
+trimul_status trimul_create(int D, int C, trimul_dtype dtype_arg, const trimul_weights* w,
                             trimul_handle** out)
 {
     if (!out) return fail(TRIMUL_ERR_INVALID_ARG, "out (handle pointer) is NULL");
     *out = nullptr;
     if (!w) return fail(TRIMUL_ERR_INVALID_ARG, "weights is NULL");
-    if (dtype != TRIMUL_BF16 && dtype != TRIMUL_FP32)
-        return fail(TRIMUL_ERR_INVALID_ARG, "dtype must be TRIMUL_BF16 or TRIMUL_FP32; got %d", (int)dtype);
+    const int dt = enum_int(&dtype_arg);
+    if (dt != TRIMUL_BF16 && dt != TRIMUL_FP32)
+        return fail(TRIMUL_ERR_INVALID_ARG, "dtype must be TRIMUL_BF16 or TRIMUL_FP32; got %d", dt);
+    const trimul_dtype dtype = (trimul_dtype)dt;
     if (!width_ok(D) || !width_ok(C))
         return fail(TRIMUL_ERR_UNSUPPORTED, "D and C must be multiples of 32 in [32, 256]; got D=%d C=%d", D, C);
     const struct { const float* p; const char* n; } req[] = {
@@ -609,31 +628,46 @@ trimul_status trimul_tune(trimul_handle* h, const void* z, const void* pair_mask
         if (e0) (void)hipEventDestroy(e0);
         return hip_fail("hipEventCreate", e);
     }
-    // Each candidate: the projection (the lean layout overwrites a while the
-    // contraction runs, so a is rebuilt first), then the contraction timed
-    // between two events; one untimed warm-up, then the best of kReps.
+    // The projection variants, each timed between two events (its output
+    // is the same for every variant), then the contraction choices, each
+    // after a fresh projection (the lean layout overwrites a while the
+    // contraction runs); one untimed warm-up, then the best of kReps.
     constexpr int kReps = 3;
-    const std::vector<trimul::Plan> cands = trimul::candidate_plans();
-    trimul::Plan best = cands[0];
-    double best_ms = 1e300;
-    for (const trimul::Plan& pl : cands) {
-        double t_min = 1e300;
+    auto time_best = [&](auto&& before, auto&& timed, double& t_min) {
+        t_min = 1e300;
         for (int r = 0; r <= kReps && e == hipSuccess; ++r) {
-            e = enq_project(h, c, stream);
+            e = before();
             if (e == hipSuccess) e = hipEventRecord(e0, stream);
-            if (e == hipSuccess) e = enq_contract(h, pl, c, stream);
+            if (e == hipSuccess) e = timed();
             if (e == hipSuccess) e = hipEventRecord(e1, stream);
             if (e == hipSuccess) e = hipEventSynchronize(e1);
             float ms = 0.f;
             if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
             if (e == hipSuccess && r > 0 && ms < t_min) t_min = ms;
         }
+    };
+    trimul::Plan best;
+    double best_k1 = 1e300, best_k2 = 1e300;
+    for (int v : trimul::k1_variants()) {
+        trimul::Plan pl = best;
+        pl.k1_variant = v;
+        double t;
+        time_best([&]() { return hipSuccess; }, [&]() { return enq_project(h, pl, c, stream); }, t);
         if (e != hipSuccess) break;
-        if (t_min < best_ms) {
-            best_ms = t_min;
-            best = pl;
-        }
+        if (t < best_k1) { best_k1 = t; best.k1_variant = v; }
     }
+    for (const trimul::Plan& k2 : trimul::k2_choices()) {
+        if (e != hipSuccess) break;
+        trimul::Plan pl = best;
+        pl.k2_order = k2.k2_order;
+        pl.k2_gm = k2.k2_gm;
+        double t;
+        time_best([&]() { return enq_project(h, pl, c, stream); }, [&]() { return enq_contract(h, pl, c, stream); },
+                  t);
+        if (e != hipSuccess) break;
+        if (t < best_k2) { best_k2 = t; best.k2_order = pl.k2_order; best.k2_gm = pl.k2_gm; }
+    }
+    const double best_ms = best_k1 + best_k2;
     (void)hipEventDestroy(e0);
     (void)hipEventDestroy(e1);
     if (e != hipSuccess) return hip_fail("tuning run", e);
@@ -655,8 +689,9 @@ trimul_status trimul_internal_project(trimul_handle* h, const void* z, const voi
 {
     if (!h) return fail(TRIMUL_ERR_INVALID_ARG, "handle is NULL");
     if (!z || !a_cm || !b_cm) return fail(TRIMUL_ERR_INVALID_ARG, "z, a_cm and b_cm must be non-NULL");
-    if (dir != TRIMUL_OUTGOING && dir != TRIMUL_INCOMING)
-        return fail(TRIMUL_ERR_INVALID_ARG, "direction must be TRIMUL_OUTGOING or TRIMUL_INCOMING; got %d", (int)dir);
+    const int d = enum_int(&dir);
+    if (!direction_ok(d))
+        return fail(TRIMUL_ERR_INVALID_ARG, "direction must be TRIMUL_OUTGOING or TRIMUL_INCOMING; got %d", d);
     trimul_status st = check_shape(h, B, N);
     if (st != TRIMUL_OK) return st;
     if (!aligned(z, 16) || !aligned(a_cm, 16) || !aligned(b_cm, 16))
@@ -664,7 +699,8 @@ trimul_status trimul_internal_project(trimul_handle* h, const void* z, const voi
     if (pair_mask && !aligned(pair_mask, 16)) return fail(TRIMUL_ERR_INVALID_ARG, "pair_mask must be 16-byte aligned");
     st = check_handle_device(h);
     if (st != TRIMUL_OK) return st;
-    hipError_t e = trimul::launch_project(h->p, z, pair_mask, B, N, dir == TRIMUL_INCOMING, a_cm, b_cm, stream);
+    const trimul::Plan plan = plan_lookup(h, {B, N, d, pair_mask ? 1 : 0});
+    hipError_t e = trimul::launch_project(h->p, plan, z, pair_mask, B, N, d == TRIMUL_INCOMING, a_cm, b_cm, stream);
     if (e != hipSuccess) return hip_fail("projection kernel launch", e);
     return ok();
 }
@@ -674,15 +710,16 @@ trimul_status trimul_internal_mask_ranges(trimul_handle* h, const void* pair_mas
 {
     if (!h) return fail(TRIMUL_ERR_INVALID_ARG, "handle is NULL");
     if (!pair_mask || !table) return fail(TRIMUL_ERR_INVALID_ARG, "pair_mask and table must be non-NULL");
-    if (dir != TRIMUL_OUTGOING && dir != TRIMUL_INCOMING)
-        return fail(TRIMUL_ERR_INVALID_ARG, "direction must be TRIMUL_OUTGOING or TRIMUL_INCOMING; got %d", (int)dir);
+    const int d = enum_int(&dir);
+    if (!direction_ok(d))
+        return fail(TRIMUL_ERR_INVALID_ARG, "direction must be TRIMUL_OUTGOING or TRIMUL_INCOMING; got %d", d);
     trimul_status st = check_shape(h, B, N);
     if (st != TRIMUL_OK) return st;
     if (!aligned(pair_mask, 16) || !aligned(table, 16))
         return fail(TRIMUL_ERR_INVALID_ARG, "pair_mask and table must be 16-byte aligned");
     st = check_handle_device(h);
     if (st != TRIMUL_OK) return st;
-    hipError_t e = trimul::launch_mask_ranges(h->p, pair_mask, B, N, dir == TRIMUL_INCOMING, table, stream);
+    hipError_t e = trimul::launch_mask_ranges(h->p, pair_mask, B, N, d == TRIMUL_INCOMING, table, stream);
     if (e != hipSuccess) return hip_fail("mask range kernel launch", e);
     return ok();
 }
@@ -696,14 +733,15 @@ trimul_status trimul_internal_contract(trimul_handle* h, const void* a_cm, const
     if (st != TRIMUL_OK) return st;
     if (!aligned(a_cm, 16) || !aligned(b_cm, 16) || !aligned(o, 16))
         return fail(TRIMUL_ERR_INVALID_ARG, "a_cm, b_cm and o must be 16-byte aligned");
-    if (dir != TRIMUL_OUTGOING && dir != TRIMUL_INCOMING)
-        return fail(TRIMUL_ERR_INVALID_ARG, "direction must be TRIMUL_OUTGOING or TRIMUL_INCOMING; got %d", (int)dir);
+    const int d = enum_int(&dir);
+    if (!direction_ok(d))
+        return fail(TRIMUL_ERR_INVALID_ARG, "direction must be TRIMUL_OUTGOING or TRIMUL_INCOMING; got %d", d);
     if (table && h->p.dtype != trimul::DType::BF16)
         return fail(TRIMUL_ERR_UNSUPPORTED, "the mask table is used by the bf16 contraction only");
     if (table && !aligned(table, 16)) return fail(TRIMUL_ERR_INVALID_ARG, "table must be 16-byte aligned");
     st = check_handle_device(h);
     if (st != TRIMUL_OK) return st;
-    const trimul::Plan plan = plan_lookup(h, {B, N, (int)dir, table ? 1 : 0});
+    const trimul::Plan plan = plan_lookup(h, {B, N, d, table ? 1 : 0});
     trimul::ContractJob job;
     job.bc0 = 0;
     job.nbc = B * h->p.C;
@@ -738,34 +776,39 @@ trimul_status trimul_internal_output(trimul_handle* h, const void* z, const void
 }
 
 trimul_status trimul_internal_set_plan(trimul_handle* h, int B, int N, trimul_direction dir, int masked,
-                                       int k2_order, int k2_gm)
+                                       int k1_variant, int k2_order, int k2_gm)
 {
     if (!h) return fail(TRIMUL_ERR_INVALID_ARG, "handle is NULL");
     trimul::PlanEntry ent;
-    ent.key = {B, N, (int)dir, masked ? 1 : 0};
+    ent.key = {B, N, enum_int(&dir), masked ? 1 : 0};
+    ent.plan.k1_variant = k1_variant;
     ent.plan.k2_order = k2_order;
     ent.plan.k2_gm = k2_gm;
     ent.ms = 0.0;
     if (!trimul::plan_valid(ent.plan))
-        return fail(TRIMUL_ERR_INVALID_ARG, "no candidate plan has k2_order=%d k2_gm=%d", k2_order, k2_gm);
+        return fail(TRIMUL_ERR_INVALID_ARG, "no candidate plan has k1_variant=%d k2_order=%d k2_gm=%d", k1_variant,
+                    k2_order, k2_gm);
     set_plan(h, ent);
     return ok();
 }
 
 trimul_status trimul_internal_get_plan(trimul_handle* h, int B, int N, trimul_direction dir, int masked,
-                                       int* k2_order, int* k2_gm)
+                                       int* k1_variant, int* k2_order, int* k2_gm)
 {
-    if (!h || !k2_order || !k2_gm) return fail(TRIMUL_ERR_INVALID_ARG, "handle and outputs must be non-NULL");
-    const trimul::Plan p = plan_lookup(h, {B, N, (int)dir, masked ? 1 : 0});
+    if (!h || !k1_variant || !k2_order || !k2_gm)
+        return fail(TRIMUL_ERR_INVALID_ARG, "handle and outputs must be non-NULL");
+    const trimul::Plan p = plan_lookup(h, {B, N, enum_int(&dir), masked ? 1 : 0});
+    *k1_variant = p.k1_variant;
     *k2_order = p.k2_order;
     *k2_gm = p.k2_gm;
     return ok();
 }
 
-int trimul_internal_plan_candidates(int* k2_order, int* k2_gm, int cap)
+int trimul_internal_plan_candidates(int* k1_variant, int* k2_order, int* k2_gm, int cap)
 {
     const std::vector<trimul::Plan> c = trimul::candidate_plans();
     for (int i = 0; i < (int)c.size() && i < cap; ++i) {
+        if (k1_variant) k1_variant[i] = c[i].k1_variant;
         if (k2_order) k2_order[i] = c[i].k2_order;
         if (k2_gm) k2_gm[i] = c[i].k2_gm;
     }
@@ -773,23 +816,26 @@ int trimul_internal_plan_candidates(int* k2_order, int* k2_gm, int cap)
 }
 
 trimul_status trimul_internal_cache_store(const char* path, const char* device, int D, int C, int dtype,
-                                          int B, int N, int dir, int masked, int k2_order, int k2_gm, double ms)
+                                          int B, int N, int dir, int masked, int k1_variant, int k2_order,
+                                          int k2_gm, double ms)
 {
     if (!path || !device) return fail(TRIMUL_ERR_INVALID_ARG, "path and device must be non-NULL");
     trimul::PlanEntry ent;
     ent.key = {B, N, dir, masked};
+    ent.plan.k1_variant = k1_variant;
     ent.plan.k2_order = k2_order;
     ent.plan.k2_gm = k2_gm;
     ent.ms = ms;
     if (!trimul::plan_valid(ent.plan))
-        return fail(TRIMUL_ERR_INVALID_ARG, "no candidate plan has k2_order=%d k2_gm=%d", k2_order, k2_gm);
+        return fail(TRIMUL_ERR_INVALID_ARG, "no candidate plan has k1_variant=%d k2_order=%d k2_gm=%d", k1_variant,
+                    k2_order, k2_gm);
     if (!trimul::plan_cache_store(path, device, D, C, dtype, ent))
         return fail(TRIMUL_ERR_INVALID_ARG, "could not write the plan cache %s", path);
     return ok();
 }
 
 int trimul_internal_cache_lookup(const char* path, const char* device, int D, int C, int dtype, int B, int N,
-                                 int dir, int masked, int* k2_order, int* k2_gm)
+                                 int dir, int masked, int* k1_variant, int* k2_order, int* k2_gm)
 {
     if (!path || !device) return -1;
     std::vector<trimul::PlanEntry> v;
@@ -797,6 +843,7 @@ int trimul_internal_cache_lookup(const char* path, const char* device, int D, in
     const trimul::PlanKey k = {B, N, dir, masked};
     for (const trimul::PlanEntry& e : v)
         if (e.key == k) {
+            if (k1_variant) *k1_variant = e.plan.k1_variant;
             if (k2_order) *k2_order = e.plan.k2_order;
             if (k2_gm) *k2_gm = e.plan.k2_gm;
             return 1;

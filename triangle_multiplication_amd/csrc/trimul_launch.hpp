@@ -61,6 +61,9 @@ struct Plan {
     int k2_order = 0;
     // Row panels per group when a channel's tiles are walked (4, 8 or 16).
     int k2_gm = 8;
+    // Projection variant.  One kernel today (two 4-wave workgroups per CU,
+    // one per 256 pairs); the field keeps the plan format stable for more.
+    int k1_variant = 0;
 };
 
 // Tile height of the bf16 contraction; the mask-range table has one entry per
@@ -100,7 +103,7 @@ struct OutputSrc {
     size_t hi_stride;
 };
 
-hipError_t launch_project(const Params& p, const void* z, const void* mask, int B, int N,
+hipError_t launch_project(const Params& p, const Plan& plan, const void* z, const void* mask, int B, int N,
                           int incoming, void* a_cm, void* b_cm, hipStream_t s);
 // Scan the pair mask for each row tile's live key range (the ranges of the
 // mask table; also clears its header).  incoming: rows of A and B are columns

@@ -28,10 +28,14 @@ struct PlanKey {
 struct PlanEntry {
     PlanKey key;
     Plan plan;
-    double ms;   // measured time of the tuned kernel with this plan
+    double ms;   // measured time of the projection and contraction with this plan
 };
 
-// Every plan trimul_tune times, the default first.
+// The projection variants and the contraction choices trimul_tune times
+// (each kernel is timed on its own, and the fastest of each kept).
+std::vector<int> k1_variants();
+std::vector<Plan> k2_choices();
+// Every combination, the default first.
 std::vector<Plan> candidate_plans();
 
 // Whether a plan is one of the candidates (plans read from a file or set by a
