@@ -52,7 +52,7 @@ def stored_traffic(name, direction, plan):
         return None
     if (t.get("workload") != name or t.get("direction") != direction
             or t.get("sources_sha256") != k2_source_digest()
-            or tuple(t.get("plan", (0, 0, 8))[1:]) != tuple(plan[1:])):
+            or tuple(t.get("plan", (0, 0, 8, 256))[1:]) != tuple(plan[1:])):
         return None
     return float(t["hbm_bytes_per_launch"])
 
@@ -150,19 +150,26 @@ def cpu_baseline(wl, z, mask, w, direction, n_sample):
     return res
 
 
-def executed_k2_flops(table, B, C, N):
-    """FLOPs the masked contraction executes: per tile pair, 2 * 256 * 256 *
-    32 per live key step (dead tiles run one step of zeros, not counted)."""
+def executed_k2_flops(table, B, C, N, tile=256):
+    """FLOPs the masked contraction executes: per tile pair, 2 * tile^2 *
+    (8192 / tile) per live key step of 8192 / tile keys (dead tiles run one
+    step of zeros, not counted).  The table's ranges are in 32-key blocks of
+    256-row tiles; a 128-row tile takes the range of the 256-row tile holding
+    it, widened to whole 64-key steps."""
     import numpy as np
     from triangle_multiplication_amd import binding
     r = binding.table_parts(table, B, N)[0].cpu().numpy()
+    kh = 256 // tile
+    nt = (N + tile - 1) // tile
     tot = 0
     for b in range(r.shape[0]):
-        lo, hi = r[b, :, 0], r[b, :, 1]
+        u = np.arange(nt) * tile // 256
+        lo, hi = r[b, u, 0], r[b, u, 1]
         L = np.maximum(lo[:, None], lo[None, :])
         H = np.minimum(hi[:, None], hi[None, :])
-        tot += int(np.clip(H - L, 0, None).sum())
-    return 2 * 256 * 256 * 32 * C * tot
+        live = H > L
+        tot += int(np.where(live, (H + kh - 1) // kh - L // kh, 0).sum())
+    return 2 * tile * tile * 32 * kh * C * tot
 
 
 def main():
@@ -344,9 +351,9 @@ def main():
                                "workload or plan differ)" % os.path.relpath(TRAFFIC_FILE, ROOT)),
             "kernel": "k2_contract",
             "per_launch": "2*B*C*N^3 = %.4g FLOP" % k2_flops, "avg_ms": round(k2_ms, 4),
-            "plan": {"k1_variant": plan[0], "k2_order": plan[1], "k2_gm": plan[2]}}
+            "plan": {"k1_variant": plan[0], "k2_order": plan[1], "k2_gm": plan[2], "k2_tile": plan[3]}}
     if use_ranges:
-        ex = executed_k2_flops(rng, B, C, N)
+        ex = executed_k2_flops(rng, B, C, N, plan[3])
         roof["executed_flops_per_launch"] = ex
         roof["executed_tflops"] = round(ex / (k2_ms * 1e-3) / 1e12, 2)
     result = {

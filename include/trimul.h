@@ -202,7 +202,8 @@ trimul_status trimul_fwd_noalloc(trimul_handle *h, const void *z, const void *pa
  * ("Environment": kept apart from the compile cache; cold and warm runs of an
  * autotuning path differ by about 2x).  Arguments, layouts and errors are
  * those of trimul_fwd.  Every candidate plan computes bitwise the same result
- * (plans only reorder whole tiles); each is run on the caller's inputs and
+ * (plans reorder or resize the contraction's tiles, and every output still sums
+ * its keys in the same order); each is run on the caller's inputs and
  * timed with HIP events, and the fastest is recorded in the handle for
  * (B, N, direction, masked) and in the plan cache file ($TRIMUL_PLAN_CACHE,
  * else $XDG_CACHE_HOME/libtrimul/plans.txt, else ~/.cache/libtrimul/plans.txt;

@@ -75,16 +75,20 @@ trimul_status trimul_internal_output(trimul_handle *h, const void *z, const void
 
 /*
  * Plans (see trimul_tune): the projection variant (only 0 today), the
- * contraction's XCD tile order (0, 1) and row-panel group (4, 8, 16).  set_plan records a plan for a call shape in the
+ * contraction's XCD tile order (0, 1), row-panel group (4, 8, 16) and tile
+ * side (256, 128).  set_plan records a plan for a call shape in the
  * handle (as trimul_tune does, without timing or writing the cache), so tests
  * can run every candidate; get_plan returns the plan trimul_fwd would use.
  * plan_candidates writes up to cap candidates and returns how many exist.
  */
 trimul_status trimul_internal_set_plan(trimul_handle *h, int B, int N, trimul_direction dir,
-                                       int masked, int k1_variant, int k2_order, int k2_gm);
+                                       int masked, int k1_variant, int k2_order, int k2_gm,
+                                       int k2_tile);
 trimul_status trimul_internal_get_plan(trimul_handle *h, int B, int N, trimul_direction dir,
-                                       int masked, int *k1_variant, int *k2_order, int *k2_gm);
-int trimul_internal_plan_candidates(int *k1_variant, int *k2_order, int *k2_gm, int cap);
+                                       int masked, int *k1_variant, int *k2_order, int *k2_gm,
+                                       int *k2_tile);
+int trimul_internal_plan_candidates(int *k1_variant, int *k2_order, int *k2_gm, int *k2_tile,
+                                    int cap);
 
 /*
  * The plan cache file, host only (no device needed): store one entry
@@ -94,10 +98,11 @@ int trimul_internal_plan_candidates(int *k1_variant, int *k2_order, int *k2_gm, 
  */
 trimul_status trimul_internal_cache_store(const char *path, const char *device, int D, int C,
                                           int dtype, int B, int N, int dir, int masked,
-                                          int k1_variant, int k2_order, int k2_gm, double ms);
+                                          int k1_variant, int k2_order, int k2_gm, int k2_tile,
+                                          double ms);
 int trimul_internal_cache_lookup(const char *path, const char *device, int D, int C, int dtype,
                                  int B, int N, int dir, int masked, int *k1_variant, int *k2_order,
-                                 int *k2_gm);
+                                 int *k2_gm, int *k2_tile);
 int trimul_internal_cache_path(char *buf, int cap);
 
 #ifdef __cplusplus

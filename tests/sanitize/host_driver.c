@@ -84,57 +84,59 @@ int main(int argc, char **argv)
     EXPECT(trimul_internal_output(NULL, dummy, dummy, 1, 64, dummy, NULL) == TRIMUL_ERR_INVALID_ARG);
     EXPECT(trimul_internal_mask_ranges(NULL, dummy, 1, 64, TRIMUL_OUTGOING, (int *)dummy, NULL) ==
            TRIMUL_ERR_INVALID_ARG);
-    int v = 0, o = 0, g = 0;
-    EXPECT(trimul_internal_get_plan(NULL, 1, 64, TRIMUL_OUTGOING, 0, &v, &o, &g) == TRIMUL_ERR_INVALID_ARG);
-    EXPECT(trimul_internal_set_plan(NULL, 1, 64, TRIMUL_OUTGOING, 0, 0, 0, 8) == TRIMUL_ERR_INVALID_ARG);
+    int v = 0, o = 0, g = 0, t = 0;
+    EXPECT(trimul_internal_get_plan(NULL, 1, 64, TRIMUL_OUTGOING, 0, &v, &o, &g, &t) == TRIMUL_ERR_INVALID_ARG);
+    EXPECT(trimul_internal_set_plan(NULL, 1, 64, TRIMUL_OUTGOING, 0, 0, 0, 8, 256) == TRIMUL_ERR_INVALID_ARG);
     trimul_destroy(NULL);
     /* plan candidates */
-    const int n = trimul_internal_plan_candidates(NULL, NULL, NULL, 0);
+    const int n = trimul_internal_plan_candidates(NULL, NULL, NULL, NULL, 0);
     EXPECT(n >= 2);
     int *cv = (int *)calloc((size_t)n, sizeof(int)), *co = (int *)calloc((size_t)n, sizeof(int)),
-        *cg = (int *)calloc((size_t)n, sizeof(int));
-    EXPECT(trimul_internal_plan_candidates(cv, co, cg, n) == n);
-    EXPECT(trimul_internal_plan_candidates(cv, co, cg, 1) == n);   /* cap respected */
+        *cg = (int *)calloc((size_t)n, sizeof(int)), *ct = (int *)calloc((size_t)n, sizeof(int));
+    EXPECT(trimul_internal_plan_candidates(cv, co, cg, ct, n) == n);
+    EXPECT(trimul_internal_plan_candidates(cv, co, cg, ct, 1) == n);   /* cap respected */
     /* plan cache file */
     char path[1024];
     snprintf(path, sizeof path, "%s/sub/dir/plans.txt", dir);
     for (int i = 0; i < n; ++i)
         EXPECT(trimul_internal_cache_store(path, "gfx950-256cu", 256, 256, 0, 1, 4096 + 8 * i, i % 2, i % 2, cv[i],
-                                           co[i], cg[i], 1.5 * i) == TRIMUL_OK);
+                                           co[i], cg[i], ct[i], 1.5 * i) == TRIMUL_OK);
     for (int i = 0; i < n; ++i) {
         EXPECT(trimul_internal_cache_lookup(path, "gfx950-256cu", 256, 256, 0, 1, 4096 + 8 * i, i % 2, i % 2, &v, &o,
-                                            &g) == 1);
-        EXPECT(v == cv[i] && o == co[i] && g == cg[i]);
+                                            &g, &t) == 1);
+        EXPECT(v == cv[i] && o == co[i] && g == cg[i] && t == ct[i]);
     }
-    EXPECT(trimul_internal_cache_lookup(path, "gfx950-256cu", 256, 256, 0, 1, 4095, 0, 0, &v, &o, &g) == 0);
+    EXPECT(trimul_internal_cache_lookup(path, "gfx950-256cu", 256, 256, 0, 1, 4095, 0, 0, &v, &o, &g, &t) == 0);
     EXPECT(trimul_internal_cache_store(path, "gfx950-256cu", 256, 256, 0, 1, 4096, 0, 0, cv[n - 1], co[n - 1],
-                                       cg[n - 1], 2.0) == TRIMUL_OK);
-    EXPECT(trimul_internal_cache_lookup(path, "gfx950-256cu", 256, 256, 0, 1, 4096, 0, 0, &v, &o, &g) == 1 &&
-           o == co[n - 1] && g == cg[n - 1]);
-    EXPECT(trimul_internal_cache_store(path, "gfx950-256cu", 256, 256, 0, 1, 64, 0, 0, 0, 3, 8, 1.0) ==
+                                       cg[n - 1], ct[n - 1], 2.0) == TRIMUL_OK);
+    EXPECT(trimul_internal_cache_lookup(path, "gfx950-256cu", 256, 256, 0, 1, 4096, 0, 0, &v, &o, &g, &t) == 1 &&
+           o == co[n - 1] && g == cg[n - 1] && t == ct[n - 1]);
+    EXPECT(trimul_internal_cache_store(path, "gfx950-256cu", 256, 256, 0, 1, 64, 0, 0, 0, 3, 8, 256, 1.0) ==
+           TRIMUL_ERR_INVALID_ARG);
+    EXPECT(trimul_internal_cache_store(path, "gfx950-256cu", 256, 256, 0, 1, 64, 0, 0, 0, 0, 8, 96, 1.0) ==
            TRIMUL_ERR_INVALID_ARG);
     {
         FILE *f = fopen(path, "a");
         if (f) {
-            fputs("trimul-plan v2 gfx950-256cu 256 256 0 1 77 0 0 0 1\n", f);   /* truncated */
-            fputs("trimul-plan v2 gfx950-256cu 256 256 0 1 78 0 0 0 1 8 nan-ish trailing junk\n", f);
+            fputs("trimul-plan v3 gfx950-256cu 256 256 0 1 77 0 0 0 1\n", f);   /* truncated */
+            fputs("trimul-plan v3 gfx950-256cu 256 256 0 1 78 0 0 0 1 8 256 nan-ish trailing junk\n", f);
             fputs("#\n\n", f);
             for (int i = 0; i < 300; ++i) fputc('z', f);   /* a long line */
             fputc('\n', f);
             fclose(f);
         }
-        EXPECT(trimul_internal_cache_lookup(path, "gfx950-256cu", 256, 256, 0, 1, 77, 0, 0, &v, &o, &g) == 0);
+        EXPECT(trimul_internal_cache_lookup(path, "gfx950-256cu", 256, 256, 0, 1, 77, 0, 0, &v, &o, &g, &t) == 0);
     }
     char blocker[1024], bad[1100];
     snprintf(blocker, sizeof blocker, "%s/blocker", dir);
     FILE *bf = fopen(blocker, "w");
     if (bf) fclose(bf);
     snprintf(bad, sizeof bad, "%s/plans.txt", blocker);
-    EXPECT(trimul_internal_cache_store(bad, "d", 32, 32, 0, 1, 64, 0, 0, 0, 0, 8, 1.0) == TRIMUL_ERR_INVALID_ARG);
-    EXPECT(trimul_internal_cache_lookup(bad, "d", 32, 32, 0, 1, 64, 0, 0, &v, &o, &g) <= 0);
+    EXPECT(trimul_internal_cache_store(bad, "d", 32, 32, 0, 1, 64, 0, 0, 0, 0, 8, 256, 1.0) == TRIMUL_ERR_INVALID_ARG);
+    EXPECT(trimul_internal_cache_lookup(bad, "d", 32, 32, 0, 1, 64, 0, 0, &v, &o, &g, &t) <= 0);
     char pbuf[8];
     EXPECT(trimul_internal_cache_path(pbuf, (int)sizeof pbuf) >= 0);   /* truncated into a small buffer */
-    free(cv); free(co); free(cg);
+    free(cv); free(co); free(cg); free(ct);
     printf("host driver: %d failures\n", failures);
     return failures ? 1 : 0;
 }

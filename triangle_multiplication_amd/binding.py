@@ -80,15 +80,15 @@ _lib.trimul_internal_contract.restype = _ci
 _lib.trimul_internal_output.argtypes = [_vp, _vp, _vp, _ci, _ci, _vp, _vp]
 _lib.trimul_internal_output.restype = _ci
 _ip = ctypes.POINTER(_ci)
-_lib.trimul_internal_set_plan.argtypes = [_vp, _ci, _ci, _ci, _ci, _ci, _ci, _ci]
+_lib.trimul_internal_set_plan.argtypes = [_vp, _ci, _ci, _ci, _ci, _ci, _ci, _ci, _ci]
 _lib.trimul_internal_set_plan.restype = _ci
-_lib.trimul_internal_get_plan.argtypes = [_vp, _ci, _ci, _ci, _ci, _ip, _ip, _ip]
+_lib.trimul_internal_get_plan.argtypes = [_vp, _ci, _ci, _ci, _ci, _ip, _ip, _ip, _ip]
 _lib.trimul_internal_get_plan.restype = _ci
-_lib.trimul_internal_plan_candidates.argtypes = [_ip, _ip, _ip, _ci]
+_lib.trimul_internal_plan_candidates.argtypes = [_ip, _ip, _ip, _ip, _ci]
 _lib.trimul_internal_plan_candidates.restype = _ci
-_lib.trimul_internal_cache_store.argtypes = [ctypes.c_char_p, ctypes.c_char_p] + [_ci] * 10 + [ctypes.c_double]
+_lib.trimul_internal_cache_store.argtypes = [ctypes.c_char_p, ctypes.c_char_p] + [_ci] * 11 + [ctypes.c_double]
 _lib.trimul_internal_cache_store.restype = _ci
-_lib.trimul_internal_cache_lookup.argtypes = [ctypes.c_char_p, ctypes.c_char_p] + [_ci] * 7 + [_ip, _ip, _ip]
+_lib.trimul_internal_cache_lookup.argtypes = [ctypes.c_char_p, ctypes.c_char_p] + [_ci] * 7 + [_ip, _ip, _ip, _ip]
 _lib.trimul_internal_cache_lookup.restype = _ci
 _lib.trimul_internal_cache_path.argtypes = [ctypes.c_char_p, _ci]
 _lib.trimul_internal_cache_path.restype = _ci
@@ -217,44 +217,44 @@ def table_parts(table, B, N):
 
 
 def trimul_internal_set_plan(h, B, N, direction, masked, plan):
-    """Record plan = (k1_variant, k2_order, k2_gm) for the call shape."""
-    k1, order, gm = plan
+    """Record plan = (k1_variant, k2_order, k2_gm, k2_tile) for the call shape."""
+    k1, order, gm, tile = plan
     _check(_lib.trimul_internal_set_plan(h, B, N, DIRECTIONS.get(direction, direction), int(bool(masked)),
-                                         k1, order, gm))
+                                         k1, order, gm, tile))
 
 
 def trimul_internal_get_plan(h, B, N, direction, masked):
-    """(k1_variant, k2_order, k2_gm) that trimul_fwd uses for the call shape."""
-    v, o, g = _ci(0), _ci(0), _ci(0)
+    """(k1_variant, k2_order, k2_gm, k2_tile) that trimul_fwd uses for the call shape."""
+    v, o, g, t = _ci(0), _ci(0), _ci(0), _ci(0)
     _check(_lib.trimul_internal_get_plan(h, B, N, DIRECTIONS.get(direction, direction), int(bool(masked)),
-                                         ctypes.byref(v), ctypes.byref(o), ctypes.byref(g)))
-    return v.value, o.value, g.value
+                                         ctypes.byref(v), ctypes.byref(o), ctypes.byref(g), ctypes.byref(t)))
+    return v.value, o.value, g.value, t.value
 
 
 def plan_candidates():
-    n = _lib.trimul_internal_plan_candidates(None, None, None, 0)
-    v, o, g = (_ci * n)(), (_ci * n)(), (_ci * n)()
-    _lib.trimul_internal_plan_candidates(v, o, g, n)
-    return [(v[i], o[i], g[i]) for i in range(n)]
+    n = _lib.trimul_internal_plan_candidates(None, None, None, None, 0)
+    v, o, g, t = (_ci * n)(), (_ci * n)(), (_ci * n)(), (_ci * n)()
+    _lib.trimul_internal_plan_candidates(v, o, g, t, n)
+    return [(v[i], o[i], g[i], t[i]) for i in range(n)]
 
 
 def cache_store(path, device, D, C, dtype, B, N, direction, masked, plan, ms):
-    k1, order, gm = plan
+    k1, order, gm, tile = plan
     _check(_lib.trimul_internal_cache_store(path.encode(), device.encode(), D, C, DTYPES.get(dtype, dtype), B, N,
                                             DIRECTIONS.get(direction, direction), int(bool(masked)),
-                                            k1, order, gm, float(ms)))
+                                            k1, order, gm, tile, float(ms)))
 
 
 def cache_lookup(path, device, D, C, dtype, B, N, direction, masked):
-    """(k1_variant, k2_order, k2_gm) recorded for the key, None if absent;
-    raises OSError if the file cannot be read."""
-    v, o, g = _ci(0), _ci(0), _ci(0)
+    """(k1_variant, k2_order, k2_gm, k2_tile) recorded for the key, None if
+    absent; raises OSError if the file cannot be read."""
+    v, o, g, t = _ci(0), _ci(0), _ci(0), _ci(0)
     r = _lib.trimul_internal_cache_lookup(path.encode(), device.encode(), D, C, DTYPES.get(dtype, dtype), B, N,
                                           DIRECTIONS.get(direction, direction), int(bool(masked)),
-                                          ctypes.byref(v), ctypes.byref(o), ctypes.byref(g))
+                                          ctypes.byref(v), ctypes.byref(o), ctypes.byref(g), ctypes.byref(t))
     if r < 0:
         raise OSError("plan cache %s cannot be read" % path)
-    return (v.value, o.value, g.value) if r else None
+    return (v.value, o.value, g.value, t.value) if r else None
 
 
 def cache_path():

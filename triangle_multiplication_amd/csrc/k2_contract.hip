@@ -245,26 +245,34 @@ struct K2PArgs {
     int order, gm;        // Plan
 };
 
-template <int NSP>
+template <int NSP, int TB>
 __global__ __launch_bounds__(512) void k2_contract_ppp(K2PArgs args)
 {
     using namespace k2big;
+    static_assert(TB == 256 || TB == 128, "tile sides");
     constexpr int NW = 8;
     constexpr int DPO = OPB / 1024 / NW;            // DMA instructions per wave per operand (2)
     constexpr int DPS = 2 * DPO;                    // per wave per step
     constexpr int DIST = NSP - 1;                   // DMA runs this many steps ahead
+    constexpr int KH = BM / TB;                     // 32-key blocks per step (1 or 2)
+    constexpr int RG = TB / 16;                     // 16-row groups of one key block
+    constexpr int WM = TB / 2, WN = TB / 4;         // a wave's block of the tile
+    constexpr int MB = WM / 16, NB = WN / 16;       // its 16 x 16 MFMA blocks
+    static_assert(NB % 2 == 0 && RG % 2 == 0, "paired column blocks and row groups");
     __shared__ __attribute__((aligned(1024))) unsigned char smem[NSP * STB];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 2, wn = wave & 3;        // group = wm
     const int N = args.N, total = args.total;
-    const size_t slab = (size_t)N * N;
-    const int tiles = (N + BM - 1) / BM;
+    const int tiles = (N + TB - 1) / TB;
     const int per_bc = tiles * tiles;
     const int G = gridDim.x, g = blockIdx.x;
     const int n_my = (total - g + G - 1) / G;       // tiles of this workgroup (g < total)
-    const int nk = (N + BK - 1) / BK;
+    const int nk = (N + BK * KH - 1) / (BK * KH);   // steps of a whole tile
+    // Live-first pair lists exist for 256-row tiles only; 128-row tiles walk
+    // the plain order and take the key range of the 256-row tiles holding them.
+    const bool use_pairs = TB == 256 && args.ranges;
 
     // Tile tl of this workgroup: virtual block vb = g + tl*G through the
     // order's map, a bijection of [0, total) (total and G are multiples of 8),
@@ -278,11 +286,11 @@ __global__ __launch_bounds__(512) void k2_contract_ppp(K2PArgs args)
     };
     // Masked: the first nbc * nl logical tiles are slots [0, nl) of every
     // slab's pair list, the rest slots [nl, tiles^2).
-    const unsigned nl = args.ranges ? (unsigned)args.hdr[0] : 0u;
+    const unsigned nl = use_pairs ? (unsigned)args.hdr[0] : 0u;
     const unsigned nbc_l = (unsigned)total / (unsigned)per_bc;
     auto tile_geo = [&](int tl, size_t& bc, int& ti, int& tj) {
         const unsigned logical = logical_of((unsigned)g + (unsigned)tl * (unsigned)G);
-        if (args.ranges) {
+        if (use_pairs) {
             unsigned p;
             if (logical < nbc_l * nl) {
                 bc = logical / nl;
@@ -306,36 +314,44 @@ __global__ __launch_bounds__(512) void k2_contract_ppp(K2PArgs args)
         tj = (t % (GM * tiles)) / gm;
     };
     // K-steps of tile (bc, ti, tj): [klo, klo + kn); kn >= 1, and dead tiles
-    // (no live step) run one step that reads zeros.
+    // (no live step) run one step that reads zeros.  The table's ranges are in
+    // 32-key blocks of 256-row tiles; a step of KH blocks is run if any of its
+    // blocks is live.
+    const int t256 = (N + BM - 1) / BM;
     auto krange = [&](size_t bc, int ti, int tj, int& klo, int& kn, bool& live) {
         if (!args.ranges) { klo = 0; kn = nk; live = true; return; }
         const int b = (int)(((size_t)args.bc0 + bc) / (size_t)args.C);
-        const int* r = args.ranges + (size_t)b * tiles * 2;
-        const int lo = max(r[2 * ti], r[2 * tj]), hi = min(r[2 * ti + 1], r[2 * tj + 1]);
+        const int* r = args.ranges + (size_t)b * t256 * 2;
+        const int ui = ti * TB / BM, uj = tj * TB / BM;
+        const int lo = max(r[2 * ui], r[2 * uj]), hi = min(r[2 * ui + 1], r[2 * uj + 1]);
         live = lo < hi;
-        klo = live ? lo : 0;
-        kn = live ? hi - lo : 1;
+        klo = live ? lo / KH : 0;
+        kn = live ? (hi + KH - 1) / KH - lo / KH : 1;
     };
 
-    // Operand slab: [nk][N][32] bf16.  DMA instruction q of a wave covers rows
-    // 16 (DPO wave + q) .. +15 of the tile, one contiguous kilobyte of the
-    // step's block; lane l reads row dr, chunk dc (the slot swizzle is
-    // applied by choosing which lane reads which chunk).
+    // Operand slab: [nk][N][32] bf16.  A slot holds, per operand, KH key
+    // blocks of TB rows (16 KB either way).  DMA instruction q of a wave fills
+    // kilobyte 2 wave + q of the operand's part: key block kh_w = (2 wave) / RG
+    // of the step, rows 16 ((2 wave + q) % RG) .. +15 of the tile, one
+    // contiguous kilobyte of the slab; lane l reads row dr, chunk dc (the slot
+    // swizzle is applied by choosing which lane reads which chunk).
     const size_t aslab = ab_slab_elems(DType::BF16, N);
     const unsigned nrec = (unsigned)(aslab * sizeof(bf16));
     const int dpos = (lane & 7) ^ (lane >> 3);
     const int dr = 2 * (lane >> 3) + (dpos >> 2), dc = dpos & 3;
     constexpr unsigned qstride = 16u * ROWB;
     const unsigned kstride = (unsigned)N * ROWB;    // bytes per K-block
-    const unsigned lane_off = (unsigned)(wave * 16 * DPO + dr) * ROWB + dc * 16u;
+    const int kh_w = (2 * wave) / RG;               // this wave's key block of a step
+    const int g32 = ((2 * wave) % RG) / 2;          // its 32-row group of the tile
+    const unsigned lane_off = (unsigned)(32 * g32 + dr) * ROWB + dc * 16u;
     // B rows are loaded permuted within each 32-row group: slot row 16 h + r
     // (h = 0, 1; r = 0..15) holds tile row 8 (r / 4) + 4 h + r % 4.  After the
     // MFMAs of blocks 2p and 2p + 1, lane group g then holds the results for
-    // rows 32 p + 8 g .. + 7 of its wave's 64, eight consecutive j of one i,
-    // stored as one 16-byte run.  Instruction q of a wave fills slot rows
-    // 16 (2 wave + q) .. + 15, i.e. h = q and group wave.
+    // rows 32 p + 8 g .. + 7 of its wave's columns, eight consecutive j of one
+    // i, stored as one 16-byte run.  Instruction q of a wave fills slot rows
+    // 16 (2 g32 + q) .. + 15, i.e. h = q and group g32.
     static_assert(DPO == 2, "B row permutation assumes two DMA instructions per operand per wave");
-    const unsigned lane_off_b = (unsigned)(32 * wave + 8 * (dr >> 2) + (dr & 3)) * ROWB + dc * 16u;
+    const unsigned lane_off_b = (unsigned)(32 * g32 + 8 * (dr >> 2) + (dr & 3)) * ROWB + dc * 16u;
 
     // DMA cursor: the next step to load is step ikk of tile itl (K-step
     // iklo + ikk).  The tile's buffer descriptors, row offsets and K range are
@@ -356,14 +372,14 @@ __global__ __launch_bounds__(512) void k2_contract_ppp(K2PArgs args)
         const size_t sb = (size_t)args.bc0 + bc;
         ra = __builtin_amdgcn_make_buffer_rsrc((void*)(args.A + sb * aslab), 0, nrec, 0x00020000);
         rb = __builtin_amdgcn_make_buffer_rsrc((void*)(args.Bm + sb * aslab), 0, nrec, 0x00020000);
-        oa_t = lane_off + (unsigned)(ti * BM) * ROWB;
-        ob_t = lane_off_b + (unsigned)(tj * BN) * ROWB;
+        oa_t = lane_off + (unsigned)(ti * TB) * ROWB;
+        ob_t = lane_off_b + (unsigned)(tj * TB) * ROWB;
     };
     set_tile();
     int isl = 0;                                    // ring slot of the next step
     auto issue = [&]() {
         unsigned char* st = smem + isl * STB + wave * DPO * 1024;
-        const int kk = iklo + ikk;
+        const int kk = (iklo + ikk) * KH + kh_w;     // key block
         const int k0 = kk * BK;
         const unsigned kb = (unsigned)kk * kstride;
         const unsigned kpen = (ilive && k0 + dc * 8 < N) ? 0u : 0x80000000u;
@@ -378,17 +394,19 @@ __global__ __launch_bounds__(512) void k2_contract_ppp(K2PArgs args)
         if (++ikk == ikn) { ikk = 0; ++itl; set_tile(); }
     };
 
+    // Fragments: key block kh of a slot starts TB rows (TB * 64 bytes) after
+    // block kh - 1 in each operand's part.
     const int rchunk = lane >> 4;
-    const int fa_base = slot_off(wm * 128 + (lane & 15), rchunk);
-    const int fb_base = OPB + slot_off(wn * 64 + (lane & 15), rchunk);
+    const int fa_base = slot_off(wm * WM + (lane & 15), rchunk);
+    const int fb_base = OPB + slot_off(wn * WN + (lane & 15), rchunk);
 
-    f32x4 acc[8][4];
+    f32x4 acc[MB][NB];
 #pragma unroll
-    for (int m = 0; m < 8; ++m)
+    for (int m = 0; m < MB; ++m)
 #pragma unroll
-        for (int n = 0; n < 4; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int n = 0; n < NB; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    u32x4 fa[8], fb[4];
+    u32x4 fa[KH][MB], fb[KH][NB];
     auto barrier = [&]() {
         __builtin_amdgcn_sched_barrier(0);
         asm volatile("" ::: "memory");
@@ -417,33 +435,40 @@ __global__ __launch_bounds__(512) void k2_contract_ppp(K2PArgs args)
         const unsigned char* st = smem + rsl * STB;
         if (++rsl == NSP) rsl = 0;
 #pragma unroll
-        for (int m = 0; m < 8; ++m) fa[m] = *reinterpret_cast<const u32x4*>(st + fa_base + m * 1024);
+        for (int kh = 0; kh < KH; ++kh) {
 #pragma unroll
-        for (int n = 0; n < 4; ++n) fb[n] = *reinterpret_cast<const u32x4*>(st + fb_base + n * 1024);
+            for (int m = 0; m < MB; ++m)
+                fa[kh][m] = *reinterpret_cast<const u32x4*>(st + kh * TB * ROWB + fa_base + m * 1024);
+#pragma unroll
+            for (int n = 0; n < NB; ++n)
+                fb[kh][n] = *reinterpret_cast<const u32x4*>(st + kh * TB * ROWB + fb_base + n * 1024);
+        }
         issue();                                        // step s + DIST
         __builtin_amdgcn_s_waitcnt(waitcnt_vm_lds0((DIST - 1) * DPS));
         barrier();
         // C_s.  Operands swapped (b rows as the MFMA's A): each lane's four
         // results are four consecutive j of one i.
 #pragma unroll
-        for (int m = 0; m < 8; ++m)
+        for (int kh = 0; kh < KH; ++kh)
 #pragma unroll
-            for (int n = 0; n < 4; ++n) acc[m][n] = Elem<bf16>::mma(fb[n], fa[m], acc[m][n]);
+            for (int m = 0; m < MB; ++m)
+#pragma unroll
+                for (int n = 0; n < NB; ++n) acc[m][n] = Elem<bf16>::mma(fb[kh][n], fa[kh][m], acc[m][n]);
         __builtin_amdgcn_s_waitcnt(waitcnt_vm((DIST - 1) * DPS));
         barrier();
         if (++kin == nk_cur) {
             // Tile tl complete: store this wave's block and start the next.
             size_t bc; int ti, tj;
             tile_geo(tl, bc, ti, tj);
-            const int i0 = ti * BM, j0 = tj * BN;
+            const int i0 = ti * TB, j0 = tj * TB;
             bf16* Ob = args.O + bc * args.o_stride;
 #pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                const int i = i0 + wm * 128 + m * 16 + (lane & 15);
+            for (int m = 0; m < MB; ++m) {
+                const int i = i0 + wm * WM + m * 16 + (lane & 15);
 #pragma unroll
-                for (int p = 0; p < 2; ++p) {
+                for (int p = 0; p < NB / 2; ++p) {
                     // j .. j + 7 (8 divides N, so all or none exist)
-                    const int j = j0 + wn * 64 + 32 * p + 8 * (lane >> 4);
+                    const int j = j0 + wn * WN + 32 * p + 8 * (lane >> 4);
                     bf16x8 h;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
@@ -477,7 +502,8 @@ __global__ __launch_bounds__(512) void k2_contract_ppp(K2PArgs args)
 // A mask value counts as live unless it compares equal to zero (-0 is zero,
 // NaN is live, so a NaN still reaches the output).
 // One 256-thread workgroup per (tile, batch element) reads the tile's mask
-// rows (outgoing) or columns (incoming) once, in 16-byte chunks.
+// rows (outgoing) or columns (incoming) once, in 16-byte chunks, eight loads
+// in flight per thread.
 // ---------------------------------------------------------------------------
 template <typename T>
 __device__ inline bool mask_live(T v) { return v != (T)0; }
@@ -493,19 +519,32 @@ __global__ __launch_bounds__(256) void k0_mask_ranges(const T* __restrict__ mask
     const T* m = mask + (size_t)b * N * N;
     const int r0 = t * K2_TILE, rows = min(N, r0 + K2_TILE) - r0;   // multiple of 8
     int kmin = 0x7fffffff, kmax = -1;
+    // Each thread keeps U independent 16-byte loads in flight; indices past the
+    // end load a valid chunk (the first) and are not counted.
+    constexpr int U = 8;
     if (!incoming) {
-        // Rows r0 .. r0 + rows - 1 of the mask, keys along the row.
-        const int nch = N / CE;
-        for (int r = 0; r < rows; ++r) {
-            const T* row = m + (size_t)(r0 + r) * N;
-            for (int c = tid; c < nch; c += 256) {
-                const u32x4 v = ld16(row + (size_t)c * CE);
-                const T* e = reinterpret_cast<const T*>(&v);
+        // Rows r0 .. r0 + rows - 1 of the mask, keys along the row: chunk
+        // idx = r * nch + c of the tile's rows.
+        const int nch = N / CE, total = rows * nch;
+        const T* tile0 = m + (size_t)r0 * N;
+        for (int base = tid; base < total; base += 256 * U) {
+            u32x4 v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int idx = min(base + u * 256, total - 1);
+                v[u] = ld16(tile0 + (size_t)(idx / nch) * N + (size_t)(idx % nch) * CE);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int idx = base + u * 256;
+                if (idx >= total) break;
+                const int key0 = (idx % nch) * CE;
+                const T* e = reinterpret_cast<const T*>(&v[u]);
 #pragma unroll
                 for (int q = 0; q < CE; ++q)
                     if (mask_live(e[q])) {
-                        kmin = min(kmin, c * CE + q);
-                        kmax = max(kmax, c * CE + q);
+                        kmin = min(kmin, key0 + q);
+                        kmax = max(kmax, key0 + q);
                     }
             }
         }
@@ -516,15 +555,25 @@ __global__ __launch_bounds__(256) void k0_mask_ranges(const T* __restrict__ mask
         const int rpi = 256 / cpr;                  // mask rows per pass
         const int c = tid % cpr, k0 = tid / cpr;
         if (k0 < rpi)
-            for (int k = k0; k < N; k += rpi) {
-                const u32x4 v = ld16(m + (size_t)k * N + r0 + c * CE);
-                const T* e = reinterpret_cast<const T*>(&v);
-                bool live = false;
+            for (int kb = k0; kb < N; kb += rpi * U) {
+                u32x4 v[U];
 #pragma unroll
-                for (int q = 0; q < CE; ++q) live |= mask_live(e[q]);
-                if (live) {
-                    kmin = min(kmin, k);
-                    kmax = max(kmax, k);
+                for (int u = 0; u < U; ++u) {
+                    const int k = min(kb + u * rpi, N - 1);
+                    v[u] = ld16(m + (size_t)k * N + r0 + c * CE);
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int k = kb + u * rpi;
+                    if (k >= N) break;
+                    const T* e = reinterpret_cast<const T*>(&v[u]);
+                    bool live = false;
+#pragma unroll
+                    for (int q = 0; q < CE; ++q) live |= mask_live(e[q]);
+                    if (live) {
+                        kmin = min(kmin, k);
+                        kmax = max(kmax, k);
+                    }
                 }
             }
     }
@@ -628,6 +677,7 @@ __global__ __launch_bounds__(256) void k0_tile_pairs(int* __restrict__ table, in
 
 hipError_t launch_tile_pairs(const Plan& plan, int* table, int B, int N, hipStream_t s)
 {
+    if (plan.k2_tile != K2_TILE) return hipSuccess;   // 128-row tiles walk the plain order
     const int tiles = (N + K2_TILE - 1) / K2_TILE;
     hipLaunchKernelGGL(k0_tile_pairs, dim3((unsigned)B), dim3(256), 0, s, table, B, tiles, plan.k2_gm);
     return hipGetLastError();
@@ -646,12 +696,12 @@ static hipError_t launch_k2(const void* a, const void* b, int N, const ContractJ
 hipError_t launch_contract(const Params& p, const Plan& plan, const void* a_cm, const void* b_cm,
                            int B, int N, const ContractJob& job, hipStream_t s)
 {
-    // bf16: the persistent 256 x 256 kernel at every N (measured faster than
-    // 128 x 128 tiles down to N = 384 as well: 0.031 against 0.036 ms for
-    // C = 128, N = 384); ragged tiles read zeros or rows whose outputs are
-    // never stored.
+    // bf16: the persistent kernel with the plan's tile side (256 by default;
+    // 128 wastes less on ragged edges at small N); ragged tiles read zeros or
+    // rows whose outputs are never stored.
     if (p.dtype == DType::BF16) {
-        const int tiles = (N + k2big::BM - 1) / k2big::BM;
+        const int TB = plan.k2_tile == 128 ? 128 : 256;
+        const int tiles = (N + TB - 1) / TB;
         const long long total = (long long)tiles * tiles * job.nbc;   // a multiple of 8: 8 | nbc
         int dev = 0, cus = 256;
         if (hipGetDevice(&dev) == hipSuccess)
@@ -673,7 +723,8 @@ hipError_t launch_contract(const Params& p, const Plan& plan, const void* a_cm, 
         a.bc0 = job.bc0;
         a.order = plan.k2_order;
         a.gm = plan.k2_gm;
-        hipLaunchKernelGGL(k2_contract_ppp<4>, dim3((unsigned)pg), dim3(512), 0, s, a);
+        if (TB == 128) hipLaunchKernelGGL((k2_contract_ppp<4, 128>), dim3((unsigned)pg), dim3(512), 0, s, a);
+        else hipLaunchKernelGGL((k2_contract_ppp<4, 256>), dim3((unsigned)pg), dim3(512), 0, s, a);
         return hipGetLastError();
     }
     return launch_k2<float, 128, 128>(a_cm, b_cm, N, job, s);

@@ -257,7 +257,7 @@ trimul::Plan plan_lookup(trimul_handle* h, const trimul::PlanKey& k)
     std::lock_guard<std::mutex> g(h->mu);
     for (const trimul::PlanEntry& e : h->plans)
         if (e.key == k) return e.plan;
-    return trimul::Plan{};
+    return trimul::default_plan(k);
 }
 
 trimul::Plan plan_for(trimul_handle* h, const FwdCall& c) { return plan_lookup(h, key_of(c)); }
@@ -661,11 +661,17 @@ trimul_status trimul_tune(trimul_handle* h, const void* z, const void* pair_mask
         trimul::Plan pl = best;
         pl.k2_order = k2.k2_order;
         pl.k2_gm = k2.k2_gm;
+        pl.k2_tile = k2.k2_tile;
         double t;
         time_best([&]() { return enq_project(h, pl, c, stream); }, [&]() { return enq_contract(h, pl, c, stream); },
                   t);
         if (e != hipSuccess) break;
-        if (t < best_k2) { best_k2 = t; best.k2_order = pl.k2_order; best.k2_gm = pl.k2_gm; }
+        if (t < best_k2) {
+            best_k2 = t;
+            best.k2_order = pl.k2_order;
+            best.k2_gm = pl.k2_gm;
+            best.k2_tile = pl.k2_tile;
+        }
     }
     const double best_ms = best_k1 + best_k2;
     (void)hipEventDestroy(e0);
@@ -776,7 +782,7 @@ trimul_status trimul_internal_output(trimul_handle* h, const void* z, const void
 }
 
 trimul_status trimul_internal_set_plan(trimul_handle* h, int B, int N, trimul_direction dir, int masked,
-                                       int k1_variant, int k2_order, int k2_gm)
+                                       int k1_variant, int k2_order, int k2_gm, int k2_tile)
 {
     if (!h) return fail(TRIMUL_ERR_INVALID_ARG, "handle is NULL");
     trimul::PlanEntry ent;
@@ -784,40 +790,43 @@ trimul_status trimul_internal_set_plan(trimul_handle* h, int B, int N, trimul_di
     ent.plan.k1_variant = k1_variant;
     ent.plan.k2_order = k2_order;
     ent.plan.k2_gm = k2_gm;
+    ent.plan.k2_tile = k2_tile;
     ent.ms = 0.0;
     if (!trimul::plan_valid(ent.plan))
-        return fail(TRIMUL_ERR_INVALID_ARG, "no candidate plan has k1_variant=%d k2_order=%d k2_gm=%d", k1_variant,
-                    k2_order, k2_gm);
+        return fail(TRIMUL_ERR_INVALID_ARG, "no candidate plan has k1_variant=%d k2_order=%d k2_gm=%d k2_tile=%d",
+                    k1_variant, k2_order, k2_gm, k2_tile);
     set_plan(h, ent);
     return ok();
 }
 
 trimul_status trimul_internal_get_plan(trimul_handle* h, int B, int N, trimul_direction dir, int masked,
-                                       int* k1_variant, int* k2_order, int* k2_gm)
+                                       int* k1_variant, int* k2_order, int* k2_gm, int* k2_tile)
 {
-    if (!h || !k1_variant || !k2_order || !k2_gm)
+    if (!h || !k1_variant || !k2_order || !k2_gm || !k2_tile)
         return fail(TRIMUL_ERR_INVALID_ARG, "handle and outputs must be non-NULL");
     const trimul::Plan p = plan_lookup(h, {B, N, enum_int(&dir), masked ? 1 : 0});
     *k1_variant = p.k1_variant;
     *k2_order = p.k2_order;
     *k2_gm = p.k2_gm;
+    *k2_tile = p.k2_tile;
     return ok();
 }
 
-int trimul_internal_plan_candidates(int* k1_variant, int* k2_order, int* k2_gm, int cap)
+int trimul_internal_plan_candidates(int* k1_variant, int* k2_order, int* k2_gm, int* k2_tile, int cap)
 {
     const std::vector<trimul::Plan> c = trimul::candidate_plans();
     for (int i = 0; i < (int)c.size() && i < cap; ++i) {
         if (k1_variant) k1_variant[i] = c[i].k1_variant;
         if (k2_order) k2_order[i] = c[i].k2_order;
         if (k2_gm) k2_gm[i] = c[i].k2_gm;
+        if (k2_tile) k2_tile[i] = c[i].k2_tile;
     }
     return (int)c.size();
 }
 
 trimul_status trimul_internal_cache_store(const char* path, const char* device, int D, int C, int dtype,
                                           int B, int N, int dir, int masked, int k1_variant, int k2_order,
-                                          int k2_gm, double ms)
+                                          int k2_gm, int k2_tile, double ms)
 {
     if (!path || !device) return fail(TRIMUL_ERR_INVALID_ARG, "path and device must be non-NULL");
     trimul::PlanEntry ent;
@@ -825,17 +834,19 @@ trimul_status trimul_internal_cache_store(const char* path, const char* device, 
     ent.plan.k1_variant = k1_variant;
     ent.plan.k2_order = k2_order;
     ent.plan.k2_gm = k2_gm;
+    ent.plan.k2_tile = k2_tile;
     ent.ms = ms;
     if (!trimul::plan_valid(ent.plan))
-        return fail(TRIMUL_ERR_INVALID_ARG, "no candidate plan has k1_variant=%d k2_order=%d k2_gm=%d", k1_variant,
-                    k2_order, k2_gm);
+        return fail(TRIMUL_ERR_INVALID_ARG, "no candidate plan has k1_variant=%d k2_order=%d k2_gm=%d k2_tile=%d",
+                    k1_variant, k2_order, k2_gm, k2_tile);
     if (!trimul::plan_cache_store(path, device, D, C, dtype, ent))
         return fail(TRIMUL_ERR_INVALID_ARG, "could not write the plan cache %s", path);
     return ok();
 }
 
 int trimul_internal_cache_lookup(const char* path, const char* device, int D, int C, int dtype, int B, int N,
-                                 int dir, int masked, int* k1_variant, int* k2_order, int* k2_gm)
+                                 int dir, int masked, int* k1_variant, int* k2_order, int* k2_gm,
+                                 int* k2_tile)
 {
     if (!path || !device) return -1;
     std::vector<trimul::PlanEntry> v;
@@ -846,6 +857,7 @@ int trimul_internal_cache_lookup(const char* path, const char* device, int D, in
             if (k1_variant) *k1_variant = e.plan.k1_variant;
             if (k2_order) *k2_order = e.plan.k2_order;
             if (k2_gm) *k2_gm = e.plan.k2_gm;
+            if (k2_tile) *k2_tile = e.plan.k2_tile;
             return 1;
         }
     return 0;

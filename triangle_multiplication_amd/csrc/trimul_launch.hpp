@@ -64,6 +64,9 @@ struct Plan {
     // Projection variant.  One kernel today (two 4-wave workgroups per CU,
     // one per 256 pairs); the field keeps the plan format stable for more.
     int k1_variant = 0;
+    // Contraction tile side: 256 (32 keys per step) or 128 (64 keys per step,
+    // a quarter of the outputs per tile; less work lost on ragged edges).
+    int k2_tile = 256;
 };
 
 // Tile height of the bf16 contraction; the mask-range table has one entry per
@@ -111,7 +114,8 @@ hipError_t launch_project(const Params& p, const Plan& plan, const void* z, cons
 hipError_t launch_mask_ranges(const Params& p, const void* mask, int B, int N, int incoming,
                               int* table, hipStream_t s);
 // Order each batch's tile pairs live-first in the walk of plan.k2_gm (the
-// pairs and header of the mask table; its ranges must be filled).
+// pairs and header of the mask table; its ranges must be filled).  Nothing
+// to do for 128-row tiles, which do not read the lists.
 hipError_t launch_tile_pairs(const Plan& plan, int* table, int B, int N, hipStream_t s);
 hipError_t launch_contract(const Params& p, const Plan& plan, const void* a_cm, const void* b_cm,
                            int B, int N, const ContractJob& job, hipStream_t s);

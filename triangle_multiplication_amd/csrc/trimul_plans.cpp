@@ -1,7 +1,7 @@
 // trimul_plans.cpp -- candidate plans and the on-disk plan cache (host only).
 //
 // File format: plain text, one entry per line, fields separated by spaces:
-//   trimul-plan v2 <device> <D> <C> <dtype> <B> <N> <dir> <masked> <k1_variant> <k2_order> <k2_gm> <ms>
+//   trimul-plan v3 <device> <D> <C> <dtype> <B> <N> <dir> <masked> <k1_variant> <k2_order> <k2_gm> <k2_tile> <ms>
 // dtype 0 = bf16, 1 = fp32; dir 0 = outgoing, 1 = incoming; masked 0 or 1.
 // Lines starting with '#' and lines that do not parse are ignored.
 #include "trimul_plans.hpp"
@@ -23,13 +23,15 @@ std::vector<int> k1_variants() { return {0}; }
 std::vector<Plan> k2_choices()
 {
     std::vector<Plan> v;
-    for (int order : {0, 1})
-        for (int gm : {8, 4, 16}) {
-            Plan p;
-            p.k2_order = order;
-            p.k2_gm = gm;
-            v.push_back(p);
-        }
+    for (int tile : {256, 128})
+        for (int order : {0, 1})
+            for (int gm : {8, 4, 16}) {
+                Plan p;
+                p.k2_order = order;
+                p.k2_gm = gm;
+                p.k2_tile = tile;
+                v.push_back(p);
+            }
     return v;
 }
 
@@ -44,10 +46,19 @@ std::vector<Plan> candidate_plans()
     return v;
 }
 
+Plan default_plan(const PlanKey& k)
+{
+    Plan p;
+    if (k.masked) p.k2_order = 1;
+    return p;
+}
+
 bool plan_valid(const Plan& p)
 {
     for (const Plan& c : candidate_plans())
-        if (c.k1_variant == p.k1_variant && c.k2_order == p.k2_order && c.k2_gm == p.k2_gm) return true;
+        if (c.k1_variant == p.k1_variant && c.k2_order == p.k2_order && c.k2_gm == p.k2_gm &&
+            c.k2_tile == p.k2_tile)
+            return true;
     return false;
 }
 
@@ -85,9 +96,10 @@ bool parse_line(const std::string& text, Line& L)
 {
     std::istringstream in(text);
     std::string tag, ver;
-    if (!(in >> tag >> ver) || tag != "trimul-plan" || ver != "v2") return false;
+    if (!(in >> tag >> ver) || tag != "trimul-plan" || ver != "v3") return false;
     if (!(in >> L.device >> L.D >> L.C >> L.dtype >> L.e.key.B >> L.e.key.N >> L.e.key.dir >>
-          L.e.key.masked >> L.e.plan.k1_variant >> L.e.plan.k2_order >> L.e.plan.k2_gm >> L.e.ms))
+          L.e.key.masked >> L.e.plan.k1_variant >> L.e.plan.k2_order >> L.e.plan.k2_gm >> L.e.plan.k2_tile >>
+          L.e.ms))
         return false;
     return plan_valid(L.e.plan) && L.e.key.B >= 1 && L.e.key.N >= 1 && (L.e.key.dir == 0 || L.e.key.dir == 1) &&
            (L.e.key.masked == 0 || L.e.key.masked == 1);
@@ -96,9 +108,9 @@ bool parse_line(const std::string& text, Line& L)
 std::string format_line(const std::string& device, int D, int C, int dtype, const PlanEntry& e)
 {
     char buf[256];
-    std::snprintf(buf, sizeof buf, "trimul-plan v2 %s %d %d %d %d %d %d %d %d %d %d %.6g", device.c_str(), D, C,
-                  dtype, e.key.B, e.key.N, e.key.dir, e.key.masked, e.plan.k1_variant, e.plan.k2_order,
-                  e.plan.k2_gm, e.ms);
+    std::snprintf(buf, sizeof buf, "trimul-plan v3 %s %d %d %d %d %d %d %d %d %d %d %d %.6g", device.c_str(), D,
+                  C, dtype, e.key.B, e.key.N, e.key.dir, e.key.masked, e.plan.k1_variant, e.plan.k2_order,
+                  e.plan.k2_gm, e.plan.k2_tile, e.ms);
     return buf;
 }
 

@@ -35,8 +35,14 @@ struct PlanEntry {
 // (each kernel is timed on its own, and the fastest of each kept).
 std::vector<int> k1_variants();
 std::vector<Plan> k2_choices();
-// Every combination, the default first.
+// Every combination, the unmasked default first.
 std::vector<Plan> candidate_plans();
+
+// The plan of a call shape nothing was recorded for: 256-row tiles in groups
+// of 8 row panels; XCD bands (order 0) unmasked, per-round XCD blocks (order
+// 1) masked, where the live-first tile lists keep all XCDs on the same
+// channels (masked N = 8192, D = C = 128: 93.7 against 96.5 ms).
+Plan default_plan(const PlanKey& k);
 
 // Whether a plan is one of the candidates (plans read from a file or set by a
 // test are checked against this before use).
