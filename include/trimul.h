@@ -28,12 +28,13 @@
  *    checked before anything is enqueued, so an error leaves no partial work.
  *    No C++ exception crosses this ABI.
  *  - LayerNorm range (bf16 handles): both LayerNorms take their statistics in
- *    one fp32 pass (var = E[v^2] - mean^2) and are applied algebraically to
- *    the raw bf16 rows.  Results stay within the bf16 tolerance (normalised
- *    max error 2e-2 against an fp64 evaluation) for rows whose |mean| is up to
- *    128 standard deviations; the cancellation grows like (mean / std)^2 and
- *    rows far beyond that lose accuracy.  fp32 handles normalise explicitly
- *    (two passes) and have no such limit.
+ *    one fp32 pass (var = E[v^2] - mean^2); the output stage applies them
+ *    algebraically to the raw bf16 rows of z (for the output gate) and o.
+ *    Results stay within the bf16 tolerance (normalised max error 2e-2
+ *    against an fp64 evaluation) for rows whose |mean| is up to 128 standard
+ *    deviations; the cancellation grows like (mean / std)^2 and rows far
+ *    beyond that lose accuracy.  fp32 handles normalise explicitly (two
+ *    passes) and have no such limit.
  */
 #ifndef TRIMUL_H
 #define TRIMUL_H

@@ -210,15 +210,14 @@ __global__ __launch_bounds__(256) void k1_project(
 // ---------------------------------------------------------------------------
 // bf16 path for D in {128, 256}: LayerNorm folded into the projection.
 //
-// With mu, rstd = 1 / sqrt(var + eps) and sd = 1 / rstd of a z row, every
-// projection output is  W (gamma (z - mu) rstd + beta) = rstd (W' z - mu S + T sd)
-// where W' is W with gamma folded in (bf16), S its row sums and T = W beta
-// (both computed at create time, each split into bf16 high and low parts).
-// The MFMA multiplies W' with the raw bf16 z held in registers; one extra
-// K-group per block (lane group 0 holds -mu_h, -mu_h, -mu_l, sd_h, sd_h, sd_l
-// against S_h, S_l, S_h, T_h, T_l, T_h) adds the rest, so no element of z is
-// normalised explicitly.  Statistics take one pass with v_dot2_f32_bf16.
-// Epilogue per output: a = (m rstd acc_p) / (1 + 2^(-log2(e) rstd acc_g)).
+// With mu and rstd = 1 / sqrt(var + eps) of a z row, every projection output
+// is  W (gamma (z - mu) rstd + beta) = W' x + T  with x = (z - mu) rstd, W' the
+// weights with gamma folded in (bf16) and T = W beta (computed at create time,
+// split into bf16 high and low parts in the correction rows).  Statistics take
+// one pass with v_dot2_f32_bf16 over the raw bf16 z held in registers; z is
+// then normalised in place (x rounded to bf16), and the MFMA multiplies W'
+// with it.  Epilogue per output: a = m (acc_p + T_p) / (1 + 2^(-log2(e)
+// (acc_g + T_g))).
 //
 // A workgroup is 4 waves of 64 pairs; a wave's pairs are two adjacent rows of
 // the K-blocked a and b times one 32-wide k block, so each channel's 64 results
@@ -240,10 +239,9 @@ struct Cfg {
     static constexpr int STAGE = 32 * D * 2;                  // bytes per weight stage
     static constexpr int DPW = STAGE / 1024 / NWV;             // DMA instructions per wave per stage
     static constexpr int EXT = 4 * CMAX * 16;                  // correction rows
-    static constexpr int SC = NWV * RB * 2 * 16 * 4;           // per-pair scales
-    static constexpr int XF = (NWV + 1) * RB * 16 * 16;        // correction fragments + zeros
+    static constexpr int SC = NWV * RB * 16 * 4;               // per-pair mask values
     static constexpr int OT = NWV * 16 * ROWS * 2;             // per-wave output tiles
-    static constexpr int LDS = NSW * STAGE + EXT + SC + XF + OT;
+    static constexpr int LDS = NSW * STAGE + EXT + SC + OT;
     static_assert(D == 128 || D == 256, "widths");
     static_assert(STAGE % (1024 * NWV) == 0, "DMA split");
 };
@@ -263,16 +261,12 @@ __global__ __launch_bounds__(256, 2) void k1_project_fold(
     unsigned char* ring = smem;
     u32x4* ext = reinterpret_cast<u32x4*>(smem + NSW * STAGE);
     float* sc = reinterpret_cast<float*>(smem + NSW * STAGE + Cf::EXT);
-    // Correction fragments: lane group 0 of block rb of wave w at
-    // xfa + (w * RB + rb) * 256 + l16 * 16; the last RB * 256 bytes are zeros,
-    // read by lane groups 1..3.
-    unsigned char* xfa = smem + NSW * STAGE + Cf::EXT + Cf::SC;
     // This wave's output tile of one stage: 16 channel rows of 64 pairs (128
     // bytes).  The 8-byte slot c of row r sits at c ^ (2 (r / 2)), so the
     // epilogue's 8-byte writes (lanes = 16 rows x 2 slots per 32 lanes) and the
     // 16-byte read-back (lanes = 2 rows x 8 chunks per 16 lanes) hit distinct
     // banks.
-    unsigned char* otile = smem + NSW * STAGE + Cf::EXT + Cf::SC + Cf::XF + (threadIdx.x >> 6) * 16 * ROWS * 2;
+    unsigned char* otile = smem + NSW * STAGE + Cf::EXT + Cf::SC + (threadIdx.x >> 6) * 16 * ROWS * 2;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, g4 = lane >> 4;
@@ -373,11 +367,9 @@ __global__ __launch_bounds__(256, 2) void k1_project_fold(
     issue(0, ring);
     issue(1, ring + STAGE);
     issue(2, ring + 2 * STAGE);   // NQ = C / 8 >= 4
-    if (wave == 0)
-#pragma unroll
-        for (int i = 0; i < RB * 16 * 16 / (64 * 16); ++i)
-            *reinterpret_cast<u32x4*>(xfa + NWV * RB * 256 + (i * 64 + lane) * 16) = u32x4{0u, 0u, 0u, 0u};
-
+    // Statistics (one v_dot2 pass over the raw bf16 row), then z is normalised
+    // in place: each lane's registers hold (z - mu) rstd of its pair rows as
+    // bf16 (RNE), the MFMA A operand.  Missing pairs hold zeros and stay zero.
     const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -396,19 +388,20 @@ __global__ __launch_bounds__(256, 2) void k1_project_fold(
         const float mu = s1 * (1.0f / D);
         const float ve = fmaxf(s2 * (1.0f / D) - mu * mu, 0.f) + eps;
         const float rstd = rsqrtf(ve);
-        const float sd = ve * rstd;
-        const __bf16 nmh = (__bf16)(-mu), nml = (__bf16)(-mu - (float)nmh);
-        const __bf16 sdh = (__bf16)sd, sdl = (__bf16)(sd - (float)sdh);
-        const __bf16 zr = (__bf16)0.0f;
-        if (g4 == 0) {
-            *reinterpret_cast<bf16x8*>(xfa + (wave * RB + rb) * 256 + l16 * 16) =
-                bf16x8{nmh, nmh, nml, sdh, sdh, sdl, zr, zr};
-            sc[((wave * RB + rb) * 2 + 0) * 16 + l16] = -rstd * LOG2E;
-            sc[((wave * RB + rb) * 2 + 1) * 16 + l16] = mval[rb] * rstd;
-        }
+        const float nmr = -mu * rstd;
+#pragma unroll
+        for (int kg = 0; kg < KG; ++kg)
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const uint32_t w = zf[rb][kg][h];
+                const bf16x2 x = {(__bf16)fmaf(__uint_as_float(w << 16), rstd, nmr),
+                                  (__bf16)fmaf(__uint_as_float(w & 0xffff0000u), rstd, nmr)};
+                zf[rb][kg][h] = __builtin_bit_cast(uint32_t, x);
+            }
+        if (g4 == 0) sc[(wave * RB + rb) * 16 + l16] = mval[rb];
     }
     // Stage 0 landed (at most the DMA of stages 1 and 2 may be outstanding),
-    // then publish it, the correction rows and the scales.
+    // then publish it, the correction rows and the mask values.
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lds0(2 * DPW));
     barrier();
 
@@ -422,35 +415,40 @@ __global__ __launch_bounds__(256, 2) void k1_project_fold(
     };
 
     const bool full = kvalid == 32;   // wave-uniform: no tail lanes
-    // Each stage runs in two halves of HB = RB / 2 pair blocks.  A half is
-    // NSTEP = KG + 1 steps: the correction K-group, then K-groups 0 .. KG-1.
-    // Step s issues the LDS reads of step s + 1 (the last step those of the
-    // next half's correction step), the half's 2 HB MFMAs of step s and,
-    // alternating with them, the arithmetic of a share of the previous half's
-    // epilogue.  Each step is a scheduling region of its own, so the sigmoid
-    // math runs under the matrix cores instead of after them.
+    // Each stage runs in two halves of HB = RB / 2 pair blocks; a half is KG
+    // steps, one per K-group.  Step s issues the LDS reads of step s + 1, the
+    // half's 2 HB MFMAs of step s and, alternating with them, the arithmetic of
+    // a share of the previous half's epilogue.  Each step is a scheduling
+    // region of its own, so the sigmoid math runs under the matrix cores
+    // instead of after them.  The last step of a stage's first half prefetches
+    // the second half's first fragments (same slot); the first half of a stage
+    // reads its own after the barrier that publishes the stage.
     constexpr int HB = RB / 2;
-    constexpr int NSTEP = KG + 1;
     constexpr int NOUT = HB * 4;   // epilogue outputs per lane per half
-    const unsigned char* xfb = xfa + (g4 == 0 ? wave * RB * 256 : NWV * RB * 256) + l16 * 16;
-    // Per-pair scales of this lane's four output pairs in every block (they do
-    // not change from stage to stage).
-    f32x4 cxr[RB], mrr[RB];
+    // Mask values of this lane's four output pairs in every block (they do not
+    // change from stage to stage).
+    f32x4 mrr[RB];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        cxr[rb] = *reinterpret_cast<const f32x4*>(sc + ((wave * RB + rb) * 2 + 0) * 16 + 4 * g4);
-        mrr[rb] = *reinterpret_cast<const f32x4*>(sc + ((wave * RB + rb) * 2 + 1) * 16 + 4 * g4);
-    }
+    for (int rb = 0; rb < RB; ++rb) mrr[rb] = *reinterpret_cast<const f32x4*>(sc + (wave * RB + rb) * 16 + 4 * g4);
+    // beta terms T = W beta of this lane's output channel (column l16 of stage
+    // q's 16 p rows and 16 g rows): T_h + T_l from the correction rows
+    // (S_h, S_l, S_h, T_h, T_l, T_h, 0, 0); the g term scaled by -log2(e).
+    auto tvals = [&](int q, float& tp, float& ntg) {
+        const u32x4 ep = ext[q * 32 + l16], eg = ext[q * 32 + 16 + l16];
+        const uint32_t p1 = ep[1], p2 = ep[2], g1 = eg[1], g2 = eg[2];
+        tp = __uint_as_float(p1 & 0xffff0000u) + __uint_as_float(p2 << 16);
+        ntg = -LOG2E * (__uint_as_float(g1 & 0xffff0000u) + __uint_as_float(g2 << 16));
+    };
     auto fence = [&]() { __builtin_amdgcn_sched_barrier(0); };
     // One epilogue output (index k of NOUT) of the half Hp whose accumulators
-    // are pp/gp; writes a block's four pairs to the output tile after its
-    // fourth output.
+    // are pp/gp: a = m (acc_p + T_p) / (1 + 2^(-log2(e) (acc_g + T_g)));
+    // writes a block's four pairs to the output tile after its fourth output.
     const int oswz = 2 * (l16 >> 1);
-    auto epi_out = [&](auto hpc, int k, const f32x4* pp, const f32x4* gp, f32x4* ov) {
+    auto epi_out = [&](auto hpc, int k, const f32x4* pp, const f32x4* gp, f32x4* ov, float tp, float ntg) {
         constexpr int HP = decltype(hpc)::value;
         const int j = k / 4, e = k % 4, rb = HP * HB + j;
-        ov[j][e] = mrr[rb][e] * pp[j][e] *
-                   __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(cxr[rb][e] * gp[j][e]));
+        ov[j][e] = mrr[rb][e] * (pp[j][e] + tp) *
+                   __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(fmaf(gp[j][e], -LOG2E, ntg)));
         if (e == 3) {
             bf16x4 h;
             h[0] = (bf16)ov[j][0]; h[1] = (bf16)ov[j][1]; h[2] = (bf16)ov[j][2]; h[3] = (bf16)ov[j][3];
@@ -478,43 +476,36 @@ __global__ __launch_bounds__(256, 2) void k1_project_fold(
             *reinterpret_cast<u32x4*>(p) = v;
         }
     };
-    // Operands of a half's correction step: the correction rows of stage q
-    // (B side, every lane the entry of its row) and the z-side correction
-    // fragments of the half's blocks (lane group 0 only; others read zeros).
-    struct Pre { u32x4 b0, b1, xe[HB]; };
-    auto load_corr = [&](auto hc, int q, Pre& pr) {
-        constexpr int H = decltype(hc)::value;
-        pr.b0 = ext[q * 32 + l16];
-        pr.b1 = ext[q * 32 + 16 + l16];
-#pragma unroll
-        for (int j = 0; j < HB; ++j) pr.xe[j] = *reinterpret_cast<const u32x4*>(xfb + (H * HB + j) * 256);
-    };
-    // One half: MFMAs of blocks H of stage q (slot sl) into ap/ag, starting from
-    // the prefetched correction operands in cur; on return cur holds the next
-    // half's (half HN of stage qn).  If EPI, the previous half (HP, stage qp,
-    // accumulators pp/gp) is finished alongside.
-    auto half = [&](auto hc, auto epic, auto hpc, auto hnc, const unsigned char* sl, int q, Pre& cur,
-                    f32x4* ap, f32x4* ag, int qp, const f32x4* pp, const f32x4* gp, int qn) {
+    // One half: MFMAs of blocks H of the stage in slot sl into ap/ag, starting
+    // from the operands in b0/b1 (second half: prefetched by the first) and
+    // leaving there the second half's (first half only).  If EPI, the previous
+    // half (HP, stage qp, accumulators pp/gp) is finished alongside.
+    auto half = [&](auto hc, auto epic, auto hpc, const unsigned char* sl, u32x4& b0, u32x4& b1, f32x4* ap,
+                    f32x4* ag, int qp, const f32x4* pp, const f32x4* gp) {
         constexpr int H = decltype(hc)::value;
         constexpr bool EPI = decltype(epic)::value;
         f32x4 ov[HB];
-        u32x4 b0 = cur.b0, b1 = cur.b1;
+        float tp = 0.f, ntg = 0.f;
+        if (EPI) tvals(qp, tp, ntg);
+        if (H == 0) {
+            b0 = wfrag(sl, 0, 0);
+            b1 = wfrag(sl, 1, 0);
+        }
 #pragma unroll
-        for (int st = 0; st < NSTEP; ++st) {
-            // Prefetch the next step's B operands (or the next half's correction step).
+        for (int st = 0; st < KG; ++st) {
+            // Prefetch the next step's B operands (the second half's first).
+            const bool pre = st + 1 < KG || H == 0;
+            const int kn = st + 1 < KG ? st + 1 : 0;
             u32x4 n0, n1;
-            Pre nx;
-            if (st + 1 < NSTEP) {
-                n0 = wfrag(sl, 0, st);
-                n1 = wfrag(sl, 1, st);
-            } else {
-                load_corr(hnc, qn, nx);
+            if (pre) {
+                n0 = wfrag(sl, 0, kn);
+                n1 = wfrag(sl, 1, kn);
             }
             // This step's MFMAs, each followed by a share of the epilogue.
-            const int lo = st * NOUT / NSTEP, hi = (st + 1) * NOUT / NSTEP;   // constants after unrolling
+            const int lo = st * NOUT / KG, hi = (st + 1) * NOUT / KG;   // constants after unrolling
 #pragma unroll
             for (int j = 0; j < HB; ++j) {
-                const u32x4 a = st == 0 ? cur.xe[j] : zf[H * HB + j][st - 1];
+                const u32x4 a = zf[H * HB + j][st];
                 if (st == 0) {
                     const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
                     ap[j] = Elem<bf16>::mma(a, b0, z4);
@@ -526,7 +517,7 @@ __global__ __launch_bounds__(256, 2) void k1_project_fold(
             }
             if (EPI) {
 #pragma unroll
-                for (int k = lo; k < hi; ++k) epi_out(hpc, k, pp, gp, ov);
+                for (int k = lo; k < hi; ++k) epi_out(hpc, k, pp, gp, ov, tp, ntg);
             }
             // Alternate MFMAs with the epilogue arithmetic inside the step.
             // The next step's LDS reads go after this step's first MFMA
@@ -539,7 +530,7 @@ __global__ __launch_bounds__(256, 2) void k1_project_fold(
                 __builtin_amdgcn_sched_group_barrier(0x0402, 3, 0);        // VALU / transcendental
             }
             fence();
-            if (st + 1 < NSTEP) { b0 = n0; b1 = n1; } else { cur = nx; }
+            if (pre) { b0 = n0; b1 = n1; }
         }
     };
     using I0 = std::integral_constant<int, 0>;
@@ -547,9 +538,8 @@ __global__ __launch_bounds__(256, 2) void k1_project_fold(
     using T_ = std::integral_constant<bool, true>;
     using F_ = std::integral_constant<bool, false>;
     f32x4 pA[HB], gA[HB], pB[HB], gB[HB];
-    Pre cur;
-    load_corr(I0{}, 0, cur);
-    half(I0{}, F_{}, I1{}, I1{}, ring, 0, cur, pA, gA, 0, pB, gB, 0);
+    u32x4 b0, b1;
+    half(I0{}, F_{}, I1{}, ring, b0, b1, pA, gA, 0, pB, gB);
     // One iteration of the stage loop: the second half of stage q (ring slot
     // S = q % NSW) and the first half of stage q + 1.  S is a constant in each
     // of the NSW unrolled copies, so every LDS address of an iteration is a
@@ -559,8 +549,7 @@ __global__ __launch_bounds__(256, 2) void k1_project_fold(
     auto iteration = [&](auto sc, int q) -> bool {
         constexpr int S = decltype(sc)::value;
         const unsigned char* sl = ring + S * STAGE;
-        const int qn = q + 1 < NQ ? q + 1 : q;
-        half(I1{}, T_{}, I0{}, I0{}, sl, q, cur, pB, gB, q, pA, gA, qn);
+        half(I1{}, T_{}, I0{}, sl, b0, b1, pB, gB, q, pA, gA);
         if (q + 1 == NQ) return true;
         // Stage q + 1 must have landed.  Every wave issues, in this order per
         // iteration: the DMA of stage q + 3 (DPW instructions, while q + 3 <
@@ -574,7 +563,7 @@ __global__ __launch_bounds__(256, 2) void k1_project_fold(
         else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lds0(2));
         barrier();
         if (q + 3 < NQ) issue(q + 3, ring + S * STAGE);   // into the slot stage q used
-        half(I0{}, T_{}, I1{}, I1{}, ring + ((S + 1) % NSW) * STAGE, q + 1, cur, pA, gA, q, pB, gB, q + 1);
+        half(I0{}, T_{}, I1{}, ring + ((S + 1) % NSW) * STAGE, b0, b1, pA, gA, q, pB, gB);
         store_tile(q);                   // the tile is complete; stage q + 1's epilogue starts after
         return false;
     };
@@ -585,8 +574,10 @@ __global__ __launch_bounds__(256, 2) void k1_project_fold(
     }
     {
         f32x4 ov[HB];
+        float tp, ntg;
+        tvals(NQ - 1, tp, ntg);
 #pragma unroll
-        for (int k = 0; k < NOUT; ++k) epi_out(I1{}, k, pB, gB, ov);
+        for (int k = 0; k < NOUT; ++k) epi_out(I1{}, k, pB, gB, ov, tp, ntg);
         store_tile(NQ - 1);
     }
 }
