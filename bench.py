@@ -60,7 +60,8 @@ def stored_traffic(name, direction, plan):
 def metric_for(wl, headline):
     if wl.name == headline:
         return HEADLINE_METRIC
-    return "TriMul fwd ms/call + TFLOP/s (%% %s MFMA peak), B=%d N=%d D=%d" % (wl.dtype, wl.B, wl.N, wl.D)
+    m = "TriMul fwd ms/call + TFLOP/s (%% %s MFMA peak), B=%d N=%d D=%d" % (wl.dtype, wl.B, wl.N, wl.D)
+    return m if wl.C == wl.D else m + " C=%d" % wl.C
 
 
 def log(*a):
@@ -178,6 +179,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=None)
+    ap.add_argument("--shape", default=None, metavar="B,N,D,C",
+                    help="time a synthetic bf16 shape (no mask, z ~ N(0,1), outgoing unless --direction) "
+                         "instead of a named workload")
     ap.add_argument("--direction", default=None, choices=[None, "outgoing", "incoming", "both"],
                     help="'both' runs the two directions in every step, in an order rotated per step")
     ap.add_argument("--cold", default="auto", choices=["auto", "on", "off"],
@@ -216,8 +220,17 @@ def main():
         return
     from triangle_multiplication_amd import binding, inputs
 
-    name = args.workload or inputs.HEADLINE
-    wl = inputs.WORKLOADS[name]
+    if args.shape:
+        try:
+            sB, sN, sD, sC = (int(x) for x in args.shape.split(","))
+        except ValueError:
+            print("--shape takes four integers B,N,D,C; got %r" % args.shape, file=sys.stderr)
+            sys.exit(2)
+        name = "shape_bf16_b%d_n%d_d%d_c%d" % (sB, sN, sD, sC)
+        wl = inputs.Workload(name, "bf16", ("outgoing",), sB, sN, sD, sC, check="grid")
+    else:
+        name = args.workload or inputs.HEADLINE
+        wl = inputs.WORKLOADS[name]
     if args.direction == "both":
         directions = ["outgoing", "incoming"]
     else:
