@@ -406,6 +406,50 @@ def test_fwd_ragged_large_tailmask(tb, direction):
     assert (out[0, n_valid:, ::89] == 0).all() and (out[0, ::89, n_valid:] == 0).all()
 
 
+@pytest.mark.parametrize("direction", ["outgoing", "incoming"])
+def test_fwd_largest_n_tailmask(tb, direction):
+    # The largest N run here: N = 16384 at D = C = 32 (about 87 GB of device
+    # memory with the full workspace).  2.7e8 pairs per batch element and 8.6e9
+    # z elements (64-bit pair offsets in every kernel), 64 x 64 contraction
+    # tiles with 4096 tile pairs in the mask table's lists, operand slabs of
+    # 512 MiB; the last floor(N/10) tokens are masked.  D = 32 selects the
+    # generic projection and output kernels.
+    wl = inputs.Workload("big_bf16_b1_n16384_d32_tailmask", "bf16", (direction,), 1, 16384, 32, 32,
+                         mask="tail10", check="grid")
+    say("largest N", direction)
+    z, mask, w = workload_inputs(wl)
+    layer = _layer(tb, w, "bf16")
+    out = layer.forward(z, mask, direction)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    err = oracle_check(z, mask, w, direction, out, full=False, extra=wl.sample_extra())
+    say("  err", err)
+    assert err <= wl.tol
+    n_valid = 16384 - 1638
+    assert (out[0, n_valid:, ::997] == 0).all() and (out[0, ::997, n_valid:] == 0).all()
+
+
+@pytest.mark.parametrize("direction", ["outgoing", "incoming"])
+def test_fwd_many_batches_full(tb, direction):
+    # Many operand slabs: B = 128 at D = C = 128 is B*C = 16384 slabs of one
+    # 64 x 64 tile each (the folded kernels), every batch element with its own
+    # tail mask row of the mask table; checked in full.
+    B, N, D = 128, 64, 128
+    say("many batches", direction)
+    w = inputs.make_weights(D, D, "bf16", random_ln=True)
+    z = inputs.make_z(B, N, D, "bf16")
+    tm = np.ones((B, N), np.float32)
+    for b in range(B):
+        tm[b, N - 1 - (b % 17):] = 0        # 1 .. 17 masked tokens, varying per batch element
+    mask = torch.from_numpy(tm[:, :, None] * tm[:, None, :]).to(torch.bfloat16)
+    layer = _layer(tb, w, "bf16")
+    out = layer.forward(z.cuda(), mask.cuda(), direction)
+    torch.cuda.synchronize()
+    err = oracle_check(z, mask, w, direction, out, full=True)
+    say("  err", err)
+    assert err <= TOL["bf16"]
+
+
 def test_workload_in_bf16_b1_n8192_d128_chains(tb):
     z, mask, w, layer, out = _run_workload(tb, "in_bf16_b1_n8192_d128_chains", "incoming")
     # padded tail rows and columns are exactly zero (beta_out = 0)
