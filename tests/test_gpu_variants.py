@@ -214,6 +214,30 @@ def test_lean_workspace_gives_the_same_bits(tb, direction, masked):
     assert e.value.status == tb.TRIMUL_ERR_WORKSPACE
 
 
+def test_lean_workspace_full_size_bitwise(tb):
+    """The lean layout at N = 8192, D = C = 128 with the chains mask (incoming):
+    16 contraction launches of 8 slabs, each later one storing its o over the
+    previous chunk's a slabs, bitwise equal to the full layout."""
+    wl = inputs.WORKLOADS["in_bf16_b1_n8192_d128_chains"]
+    direction = "incoming"
+    say("lean full size")
+    z = inputs.make_z(wl.B, wl.N, wl.D, wl.dtype, var=wl.z_var, device="cuda")
+    mask = inputs.pair_mask(wl.token_mask(), wl.B, wl.dtype, device="cuda")
+    layer = tb.TriMul(inputs.make_weights(wl.D, wl.C, wl.dtype), wl.dtype)
+    ref = layer.forward(z, mask, direction)
+    torch.cuda.synchronize()
+    layer._ws = None
+    torch.cuda.empty_cache()
+    lean_b = tb.trimul_workspace_size_lean(layer.h, wl.B, wl.N)
+    # o keeps a region of 8 slabs (one chunk) of its own instead of C = 128
+    assert tb.trimul_workspace_size(layer.h, wl.B, wl.N) - lean_b == (wl.C - 8) * wl.N * wl.N * 2
+    ws = torch.empty(lean_b, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(z)
+    tb.trimul_fwd(layer.h, z, mask, direction, out, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+
+
 def test_tune_records_a_plan_and_the_cache_reloads_it(tb, tmp_path):
     B, N, D = 1, 1288, 128
     direction = "incoming"

@@ -67,8 +67,17 @@ def test_noalloc_refuses_shapes_beyond_its_scratch(tb):
 
 
 def test_noalloc_largest_shape_fits(tb):
-    """The documented limit: at D = C = 128, B = 1, N = 416 fits and N = 424 does not."""
-    w = inputs.make_weights(128, 128, "bf16")
+    """The documented limit: at D = C = 128, B = 1, N = 416 fits and N = 424 does
+    not; the largest shape runs and matches trimul_fwd bit for bit."""
+    w = inputs.make_weights(128, 128, "bf16", random_ln=True)
     layer = tb.TriMul(w, "bf16")
     assert tb.trimul_workspace_size(layer.h, 1, 416) <= tb.NOALLOC_MAX_BYTES
     assert tb.trimul_workspace_size_lean(layer.h, 1, 424) > tb.NOALLOC_MAX_BYTES
+    for direction in ("outgoing", "incoming"):
+        say("noalloc largest", direction)
+        z, mask = _case(416, 128, True, 23)
+        ref = layer.forward(z, mask, direction)
+        out = torch.full_like(z, float("nan"))
+        tb.trimul_fwd_noalloc(layer.h, z, mask, direction, out)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
