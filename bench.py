@@ -121,17 +121,26 @@ def cpu_baseline(wl, z, mask, w, direction, n_sample):
     if N <= 512:
         zf = z.float().cpu().numpy()
         mf = None if mask is None else mask.float().cpu().numpy()
-        t0 = time.perf_counter()
-        oracle.trimul_full(zf, mf, w, direction)
-        t_all = time.perf_counter() - t0
+
+        def per_call():
+            # whole calls, repeated until they add up to at least 2 s; the mean
+            n, t0 = 0, time.perf_counter()
+            while True:
+                oracle.trimul_full(zf, mf, w, direction)
+                n += 1
+                t = time.perf_counter() - t0
+                if t >= 2.0:
+                    return t / n, n
+
+        t_all, reps = per_call()
         res.update(value=wl.flops() / t_all / 1e12, seconds_per_call=t_all,
-                   sample="the whole call (all B*N^2 outputs), %.2f s on %d threads" % (t_all, threads))
+                   sample="the whole call (all B*N^2 outputs), mean of %d calls: %.4g s per call on %d threads"
+                          % (reps, t_all, threads))
         if _omp_set_threads(1):
-            t0 = time.perf_counter()
-            oracle.trimul_full(zf, mf, w, direction)
-            t_one = time.perf_counter() - t0
+            t_one, reps1 = per_call()
             _omp_set_threads(threads)
-            res.update(value_1thread=wl.flops() / t_one / 1e12, seconds_per_call_1thread=t_one)
+            res.update(value_1thread=wl.flops() / t_one / 1e12, seconds_per_call_1thread=t_one,
+                       calls_1thread=reps1)
         return res
     I, J = inputs.sample_grid(N, n_sample, extra=wl.sample_extra())
     zA, mA, zB, mB, zG = oracle.gather_grid(z, mask, 0, I, J, direction)
