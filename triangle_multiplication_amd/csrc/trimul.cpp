@@ -41,23 +41,47 @@ static __device__ __align__(256) unsigned char scratch[TRIMUL_NOALLOC_MAX_BYTES]
 
 namespace {
 
-thread_local std::string g_err;
+// The last error message of this thread: a fixed buffer, so that reporting
+// an error never allocates (and never throws).
+thread_local char g_err[512];
 
 trimul_status fail(trimul_status s, const char* fmt, ...)
 {
-    char buf[512];
     va_list ap;
     va_start(ap, fmt);
-    vsnprintf(buf, sizeof buf, fmt, ap);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
     va_end(ap);
-    g_err = buf;
     return s;
 }
 
 trimul_status ok()
 {
-    g_err.clear();
+    g_err[0] = '\0';
     return TRIMUL_OK;
+}
+
+// No C++ exception crosses the C ABI: entry points whose host code allocates
+// (packing, plan lists, the cache file) run through these, which turn any
+// exception (in practice std::bad_alloc) into an error status.
+template <typename F>
+trimul_status guarded(F&& f) noexcept
+{
+    try {
+        return f();
+    } catch (...) {
+        return fail(TRIMUL_ERR_INVALID_ARG, "host-side failure (out of host memory?)");
+    }
+}
+
+template <typename F>
+int guarded_int(F&& f, int on_error) noexcept
+{
+    try {
+        return f();
+    } catch (...) {
+        fail(TRIMUL_ERR_INVALID_ARG, "host-side failure (out of host memory?)");
+        return on_error;
+    }
 }
 
 trimul_status hip_fail(const char* what, hipError_t e)
@@ -409,7 +433,7 @@ const char* trimul_status_string(trimul_status s)
     return "TRIMUL_ERR_UNKNOWN";
 }
 
-const char* trimul_last_error(void) { return g_err.c_str(); }
+const char* trimul_last_error(void) { return g_err; }
 
 trimul_status trimul_check_arch(const char* name)
 {
@@ -449,134 +473,141 @@ trimul_status trimul_workspace_size_lean(const trimul_handle* h, int B, int N, s
 trimul_status trimul_create(int D, int C, trimul_dtype dtype_arg, const trimul_weights* w,
                             trimul_handle** out)
 {
-    if (!out) return fail(TRIMUL_ERR_INVALID_ARG, "out (handle pointer) is NULL");
-    *out = nullptr;
-    if (!w) return fail(TRIMUL_ERR_INVALID_ARG, "weights is NULL");
-    const int dt = enum_int(&dtype_arg);
-    if (dt != TRIMUL_BF16 && dt != TRIMUL_FP32)
-        return fail(TRIMUL_ERR_INVALID_ARG, "dtype must be TRIMUL_BF16 or TRIMUL_FP32; got %d", dt);
-    const trimul_dtype dtype = (trimul_dtype)dt;
-    if (!width_ok(D) || !width_ok(C))
-        return fail(TRIMUL_ERR_UNSUPPORTED, "D and C must be multiples of 32 in [32, 256]; got D=%d C=%d", D, C);
-    const struct { const float* p; const char* n; } req[] = {
-        {w->norm_in_weight, "norm_in_weight"}, {w->norm_in_bias, "norm_in_bias"},
-        {w->p_in, "p_in"}, {w->g_in, "g_in"}, {w->norm_out_weight, "norm_out_weight"},
-        {w->norm_out_bias, "norm_out_bias"}, {w->p_out, "p_out"}, {w->g_out, "g_out"}};
-    for (const auto& r : req)
-        if (!r.p) return fail(TRIMUL_ERR_INVALID_ARG, "weights->%s is NULL", r.n);
-    if (!(w->eps > 0.0f) || !std::isfinite(w->eps))
-        return fail(TRIMUL_ERR_INVALID_ARG, "eps must be finite and > 0; got %g", (double)w->eps);
+    return guarded([&]() -> trimul_status {
+        if (!out) return fail(TRIMUL_ERR_INVALID_ARG, "out (handle pointer) is NULL");
+        *out = nullptr;
+        if (!w) return fail(TRIMUL_ERR_INVALID_ARG, "weights is NULL");
+        const int dt = enum_int(&dtype_arg);
+        if (dt != TRIMUL_BF16 && dt != TRIMUL_FP32)
+            return fail(TRIMUL_ERR_INVALID_ARG, "dtype must be TRIMUL_BF16 or TRIMUL_FP32; got %d", dt);
+        const trimul_dtype dtype = (trimul_dtype)dt;
+        if (!width_ok(D) || !width_ok(C))
+            return fail(TRIMUL_ERR_UNSUPPORTED, "D and C must be multiples of 32 in [32, 256]; got D=%d C=%d", D, C);
+        const struct { const float* p; const char* n; } req[] = {
+            {w->norm_in_weight, "norm_in_weight"}, {w->norm_in_bias, "norm_in_bias"},
+            {w->p_in, "p_in"}, {w->g_in, "g_in"}, {w->norm_out_weight, "norm_out_weight"},
+            {w->norm_out_bias, "norm_out_bias"}, {w->p_out, "p_out"}, {w->g_out, "g_out"}};
+        for (const auto& r : req)
+            if (!r.p) return fail(TRIMUL_ERR_INVALID_ARG, "weights->%s is NULL", r.n);
+        if (!(w->eps > 0.0f) || !std::isfinite(w->eps))
+            return fail(TRIMUL_ERR_INVALID_ARG, "eps must be finite and > 0; got %g", (double)w->eps);
 
-    int dev = -1;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return hip_fail("hipGetDevice", e);
-    hipDeviceProp_t prop;
-    e = hipGetDeviceProperties(&prop, dev);
-    if (e != hipSuccess) return hip_fail("hipGetDeviceProperties", e);
-    trimul_status st = trimul_check_arch(prop.gcnArchName);
-    if (st != TRIMUL_OK) return st;
-    void* scratch_ptr = nullptr;
-    st = scratch_address(dev, &scratch_ptr);
-    if (st != TRIMUL_OK) return st;
+        int dev = -1;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return hip_fail("hipGetDevice", e);
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess) return hip_fail("hipGetDeviceProperties", e);
+        trimul_status st = trimul_check_arch(prop.gcnArchName);
+        if (st != TRIMUL_OK) return st;
+        void* scratch_ptr = nullptr;
+        st = scratch_address(dev, &scratch_ptr);
+        if (st != TRIMUL_OK) return st;
 
-    // Host packing.
-    const size_t es = elem_size(dtype);
-    const size_t n_proj = (size_t)4 * C * D, n_go = (size_t)D * D, n_po = (size_t)D * C;
-    const size_t off_proj = 0;
-    const size_t off_go = align256(n_proj * es);
-    const size_t off_po = off_go + align256(n_go * es);
-    const size_t off_ln = off_po + align256(n_po * es);
-    const size_t off_gof = off_ln + align256((size_t)(2 * D + 2 * C) * 4);
-    const bool folded = dtype == TRIMUL_BF16;
-    const size_t off_pof = off_gof + (folded ? align256(n_go * 2) : 0);
-    const size_t off_xg = off_pof + (folded ? align256(n_po * 2) : 0);
-    const size_t off_xp = off_xg + (folded ? align256((size_t)D * 16) : 0);
-    const size_t off_wpf = off_xp + (folded ? align256((size_t)D * 16) : 0);
-    const size_t off_xpj = off_wpf + (folded ? align256(n_proj * 2) : 0);
-    const size_t off_sink = off_xpj + (folded ? align256((size_t)4 * C * 16) : 0);
-    const size_t total = off_sink + 4096;
-    std::vector<uint8_t> host(total, 0);
-    if (folded) {
-        fold_rows(w->g_out, w->norm_in_weight, w->norm_in_bias, D, D,
-                  reinterpret_cast<uint16_t*>(host.data() + off_gof),
-                  reinterpret_cast<uint16_t*>(host.data() + off_xg));
-        fold_rows(w->p_out, w->norm_out_weight, w->norm_out_bias, D, C,
-                  reinterpret_cast<uint16_t*>(host.data() + off_pof),
-                  reinterpret_cast<uint16_t*>(host.data() + off_xp));
-    }
-    {
-        std::vector<uint8_t> go(n_go * es), po(n_po * es);
-        // Projection rows in the kernels' order: for a then b, per 16-channel
-        // group, 16 rows of p_in then the same channels' 16 rows of g_in.
-        std::vector<float> projf(n_proj);
-        size_t row = 0;
-        for (int part = 0; part < 2; ++part)          // a, then b
-            for (int g = 0; g < C / 16; ++g) {        // 16-channel groups
-                for (int r = 0; r < 16; ++r, ++row)   // p rows
-                    std::memcpy(&projf[row * D], w->p_in + ((size_t)part * C + g * 16 + r) * D, D * 4);
-                for (int r = 0; r < 16; ++r, ++row)   // g rows of the same channels
-                    std::memcpy(&projf[row * D], w->g_in + ((size_t)part * C + g * 16 + r) * D, D * 4);
-            }
-        std::vector<uint8_t> proj(n_proj * es);
-        for (size_t i = 0; i < n_proj; ++i) put(proj, i, projf[i], dtype);
-        if (folded)
-            fold_rows(projf.data(), w->norm_in_weight, w->norm_in_bias, 4 * C, D,
-                      reinterpret_cast<uint16_t*>(host.data() + off_wpf),
-                      reinterpret_cast<uint16_t*>(host.data() + off_xpj));
-        for (size_t i = 0; i < n_go; ++i) put(go, i, w->g_out[i], dtype);
-        for (size_t i = 0; i < n_po; ++i) put(po, i, w->p_out[i], dtype);
-        std::memcpy(host.data() + off_proj, proj.data(), proj.size());
-        std::memcpy(host.data() + off_go, go.data(), go.size());
-        std::memcpy(host.data() + off_po, po.data(), po.size());
-        float* ln = reinterpret_cast<float*>(host.data() + off_ln);
-        std::memcpy(ln, w->norm_in_weight, D * 4);
-        std::memcpy(ln + D, w->norm_in_bias, D * 4);
-        std::memcpy(ln + 2 * D, w->norm_out_weight, C * 4);
-        std::memcpy(ln + 2 * D + C, w->norm_out_bias, C * 4);
-    }
+        // Host packing.
+        const size_t es = elem_size(dtype);
+        const size_t n_proj = (size_t)4 * C * D, n_go = (size_t)D * D, n_po = (size_t)D * C;
+        const size_t off_proj = 0;
+        const size_t off_go = align256(n_proj * es);
+        const size_t off_po = off_go + align256(n_go * es);
+        const size_t off_ln = off_po + align256(n_po * es);
+        const size_t off_gof = off_ln + align256((size_t)(2 * D + 2 * C) * 4);
+        const bool folded = dtype == TRIMUL_BF16;
+        const size_t off_pof = off_gof + (folded ? align256(n_go * 2) : 0);
+        const size_t off_xg = off_pof + (folded ? align256(n_po * 2) : 0);
+        const size_t off_xp = off_xg + (folded ? align256((size_t)D * 16) : 0);
+        const size_t off_wpf = off_xp + (folded ? align256((size_t)D * 16) : 0);
+        const size_t off_xpj = off_wpf + (folded ? align256(n_proj * 2) : 0);
+        const size_t off_sink = off_xpj + (folded ? align256((size_t)4 * C * 16) : 0);
+        const size_t total = off_sink + 4096;
+        std::vector<uint8_t> host(total, 0);
+        if (folded) {
+            fold_rows(w->g_out, w->norm_in_weight, w->norm_in_bias, D, D,
+                      reinterpret_cast<uint16_t*>(host.data() + off_gof),
+                      reinterpret_cast<uint16_t*>(host.data() + off_xg));
+            fold_rows(w->p_out, w->norm_out_weight, w->norm_out_bias, D, C,
+                      reinterpret_cast<uint16_t*>(host.data() + off_pof),
+                      reinterpret_cast<uint16_t*>(host.data() + off_xp));
+        }
+        {
+            std::vector<uint8_t> go(n_go * es), po(n_po * es);
+            // Projection rows in the kernels' order: for a then b, per 16-channel
+            // group, 16 rows of p_in then the same channels' 16 rows of g_in.
+            std::vector<float> projf(n_proj);
+            size_t row = 0;
+            for (int part = 0; part < 2; ++part)          // a, then b
+                for (int g = 0; g < C / 16; ++g) {        // 16-channel groups
+                    for (int r = 0; r < 16; ++r, ++row)   // p rows
+                        std::memcpy(&projf[row * D], w->p_in + ((size_t)part * C + g * 16 + r) * D, D * 4);
+                    for (int r = 0; r < 16; ++r, ++row)   // g rows of the same channels
+                        std::memcpy(&projf[row * D], w->g_in + ((size_t)part * C + g * 16 + r) * D, D * 4);
+                }
+            std::vector<uint8_t> proj(n_proj * es);
+            for (size_t i = 0; i < n_proj; ++i) put(proj, i, projf[i], dtype);
+            if (folded)
+                fold_rows(projf.data(), w->norm_in_weight, w->norm_in_bias, 4 * C, D,
+                          reinterpret_cast<uint16_t*>(host.data() + off_wpf),
+                          reinterpret_cast<uint16_t*>(host.data() + off_xpj));
+            for (size_t i = 0; i < n_go; ++i) put(go, i, w->g_out[i], dtype);
+            for (size_t i = 0; i < n_po; ++i) put(po, i, w->p_out[i], dtype);
+            std::memcpy(host.data() + off_proj, proj.data(), proj.size());
+            std::memcpy(host.data() + off_go, go.data(), go.size());
+            std::memcpy(host.data() + off_po, po.data(), po.size());
+            float* ln = reinterpret_cast<float*>(host.data() + off_ln);
+            std::memcpy(ln, w->norm_in_weight, D * 4);
+            std::memcpy(ln + D, w->norm_in_bias, D * 4);
+            std::memcpy(ln + 2 * D, w->norm_out_weight, C * 4);
+            std::memcpy(ln + 2 * D + C, w->norm_out_bias, C * 4);
+        }
 
-    void* mem = nullptr;
-    e = hipMalloc(&mem, total);
-    if (e != hipSuccess) return hip_fail("hipMalloc (packed weights)", e);
-    e = hipMemcpy(mem, host.data(), total, hipMemcpyHostToDevice);
-    if (e != hipSuccess) {
-        (void)hipFree(mem);
-        return hip_fail("hipMemcpy (packed weights)", e);
-    }
-    trimul_handle* h = new (std::nothrow) trimul_handle;
-    if (!h) {
-        (void)hipFree(mem);
-        return fail(TRIMUL_ERR_INVALID_ARG, "out of host memory");
-    }
-    uint8_t* base = static_cast<uint8_t*>(mem);
-    h->dev_mem = mem;
-    h->device = dev;
-    h->p.D = D;
-    h->p.C = C;
-    h->p.dtype = dtype == TRIMUL_BF16 ? trimul::DType::BF16 : trimul::DType::FP32;
-    h->p.eps = w->eps;
-    h->p.w_proj = base + off_proj;
-    h->p.w_gout = base + off_go;
-    h->p.w_pout = base + off_po;
-    const float* ln = reinterpret_cast<const float*>(base + off_ln);
-    h->p.ln_in_w = ln;
-    h->p.ln_in_b = ln + D;
-    h->p.ln_out_w = ln + 2 * D;
-    h->p.ln_out_b = ln + 2 * D + C;
-    h->p.w_gout_f = folded ? base + off_gof : nullptr;
-    h->p.w_pout_f = folded ? base + off_pof : nullptr;
-    h->p.x_gout = folded ? base + off_xg : nullptr;
-    h->p.x_pout = folded ? base + off_xp : nullptr;
-    h->p.w_proj_f = folded ? base + off_wpf : nullptr;
-    h->p.x_proj = folded ? base + off_xpj : nullptr;
-    h->p.sink = base + off_sink;
-    h->scratch = scratch_ptr;
-    h->arch = trimul::plan_device_key(prop.gcnArchName, prop.multiProcessorCount);
-    // Plans recorded by trimul_tune in an earlier process (an unreadable cache
-    // only means no recorded plans).
-    (void)trimul::plan_cache_load(trimul::plan_cache_path(), h->arch, D, C, (int)dtype, h->plans);
-    *out = h;
-    return ok();
+        // Everything that can throw happens before the device allocation: the
+        // device key, and the plans recorded by trimul_tune in an earlier
+        // process (an unreadable cache only means no recorded plans).
+        std::string arch = trimul::plan_device_key(prop.gcnArchName, prop.multiProcessorCount);
+        std::vector<trimul::PlanEntry> plans;
+        (void)trimul::plan_cache_load(trimul::plan_cache_path(), arch, D, C, (int)dtype, plans);
+
+        void* mem = nullptr;
+        e = hipMalloc(&mem, total);
+        if (e != hipSuccess) return hip_fail("hipMalloc (packed weights)", e);
+        e = hipMemcpy(mem, host.data(), total, hipMemcpyHostToDevice);
+        if (e != hipSuccess) {
+            (void)hipFree(mem);
+            return hip_fail("hipMemcpy (packed weights)", e);
+        }
+        trimul_handle* h = new (std::nothrow) trimul_handle;
+        if (!h) {
+            (void)hipFree(mem);
+            return fail(TRIMUL_ERR_INVALID_ARG, "out of host memory");
+        }
+        uint8_t* base = static_cast<uint8_t*>(mem);
+        h->dev_mem = mem;
+        h->device = dev;
+        h->p.D = D;
+        h->p.C = C;
+        h->p.dtype = dtype == TRIMUL_BF16 ? trimul::DType::BF16 : trimul::DType::FP32;
+        h->p.eps = w->eps;
+        h->p.w_proj = base + off_proj;
+        h->p.w_gout = base + off_go;
+        h->p.w_pout = base + off_po;
+        const float* ln = reinterpret_cast<const float*>(base + off_ln);
+        h->p.ln_in_w = ln;
+        h->p.ln_in_b = ln + D;
+        h->p.ln_out_w = ln + 2 * D;
+        h->p.ln_out_b = ln + 2 * D + C;
+        h->p.w_gout_f = folded ? base + off_gof : nullptr;
+        h->p.w_pout_f = folded ? base + off_pof : nullptr;
+        h->p.x_gout = folded ? base + off_xg : nullptr;
+        h->p.x_pout = folded ? base + off_xp : nullptr;
+        h->p.w_proj_f = folded ? base + off_wpf : nullptr;
+        h->p.x_proj = folded ? base + off_xpj : nullptr;
+        h->p.sink = base + off_sink;
+        h->scratch = scratch_ptr;
+        h->arch = std::move(arch);
+        h->plans = std::move(plans);
+        *out = h;
+        return ok();
+    });
 }
 
 void trimul_destroy(trimul_handle* h)
@@ -618,75 +649,81 @@ trimul_status trimul_tune(trimul_handle* h, const void* z, const void* pair_mask
                           trimul_direction dir, void* out, void* workspace, size_t workspace_bytes,
                           hipStream_t stream)
 {
-    FwdCall c;
-    trimul_status st = prepare_fwd(h, z, pair_mask, B, N, dir, out, workspace, workspace_bytes, c);
-    if (st != TRIMUL_OK) return st;
-    hipEvent_t e0 = nullptr, e1 = nullptr;
-    hipError_t e = hipEventCreate(&e0);
-    if (e == hipSuccess) e = hipEventCreate(&e1);
-    if (e != hipSuccess) {
-        if (e0) (void)hipEventDestroy(e0);
-        return hip_fail("hipEventCreate", e);
-    }
-    // The projection variants, each timed between two events (its output
-    // is the same for every variant), then the contraction choices, each
-    // after a fresh projection (the lean layout overwrites a while the
-    // contraction runs); one untimed warm-up, then the best of kReps.
-    constexpr int kReps = 3;
-    auto time_best = [&](auto&& before, auto&& timed, double& t_min) {
-        t_min = 1e300;
-        for (int r = 0; r <= kReps && e == hipSuccess; ++r) {
-            e = before();
-            if (e == hipSuccess) e = hipEventRecord(e0, stream);
-            if (e == hipSuccess) e = timed();
-            if (e == hipSuccess) e = hipEventRecord(e1, stream);
-            if (e == hipSuccess) e = hipEventSynchronize(e1);
-            float ms = 0.f;
-            if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
-            if (e == hipSuccess && r > 0 && ms < t_min) t_min = ms;
+    return guarded([&]() -> trimul_status {
+        FwdCall c;
+        trimul_status st = prepare_fwd(h, z, pair_mask, B, N, dir, out, workspace, workspace_bytes, c);
+        if (st != TRIMUL_OK) return st;
+        hipEvent_t e0 = nullptr, e1 = nullptr;
+        hipError_t e = hipEventCreate(&e0);
+        if (e == hipSuccess) e = hipEventCreate(&e1);
+        if (e != hipSuccess) {
+            if (e0) (void)hipEventDestroy(e0);
+            return hip_fail("hipEventCreate", e);
         }
-    };
-    trimul::Plan best;
-    double best_k1 = 1e300, best_k2 = 1e300;
-    for (int v : trimul::k1_variants()) {
-        trimul::Plan pl = best;
-        pl.k1_variant = v;
-        double t;
-        time_best([&]() { return hipSuccess; }, [&]() { return enq_project(h, pl, c, stream); }, t);
-        if (e != hipSuccess) break;
-        if (t < best_k1) { best_k1 = t; best.k1_variant = v; }
-    }
-    for (const trimul::Plan& k2 : trimul::k2_choices()) {
-        if (e != hipSuccess) break;
-        trimul::Plan pl = best;
-        pl.k2_order = k2.k2_order;
-        pl.k2_gm = k2.k2_gm;
-        pl.k2_tile = k2.k2_tile;
-        double t;
-        time_best([&]() { return enq_project(h, pl, c, stream); }, [&]() { return enq_contract(h, pl, c, stream); },
-                  t);
-        if (e != hipSuccess) break;
-        if (t < best_k2) {
-            best_k2 = t;
-            best.k2_order = pl.k2_order;
-            best.k2_gm = pl.k2_gm;
-            best.k2_tile = pl.k2_tile;
+        // The projection variants, each timed between two events (its output
+        // is the same for every variant), then the contraction choices, each
+        // after a fresh projection (the lean layout overwrites a while the
+        // contraction runs); one untimed warm-up, then the best of kReps.
+        constexpr int kReps = 3;
+        auto time_best = [&](auto&& before, auto&& timed, double& t_min) {
+            t_min = 1e300;
+            for (int r = 0; r <= kReps && e == hipSuccess; ++r) {
+                e = before();
+                if (e == hipSuccess) e = hipEventRecord(e0, stream);
+                if (e == hipSuccess) e = timed();
+                if (e == hipSuccess) e = hipEventRecord(e1, stream);
+                if (e == hipSuccess) e = hipEventSynchronize(e1);
+                float ms = 0.f;
+                if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+                if (e == hipSuccess && r > 0 && ms < t_min) t_min = ms;
+            }
+        };
+        trimul::Plan best;
+        double best_k1 = 1e300, best_k2 = 1e300;
+        for (int v : trimul::k1_variants()) {
+            trimul::Plan pl = best;
+            pl.k1_variant = v;
+            double t;
+            time_best([&]() { return hipSuccess; }, [&]() { return enq_project(h, pl, c, stream); }, t);
+            if (e != hipSuccess) break;
+            if (t < best_k1) { best_k1 = t; best.k1_variant = v; }
         }
-    }
-    const double best_ms = best_k1 + best_k2;
-    (void)hipEventDestroy(e0);
-    (void)hipEventDestroy(e1);
-    if (e != hipSuccess) return hip_fail("tuning run", e);
-    trimul::PlanEntry ent;
-    ent.key = key_of(c);
-    ent.plan = best;
-    ent.ms = best_ms;
-    set_plan(h, ent);
-    // The cache is best effort: a read-only or missing location only means the
-    // next process tunes again.
-    (void)trimul::plan_cache_store(trimul::plan_cache_path(), h->arch, h->p.D, h->p.C, (int)h->p.dtype, ent);
-    // Leave a correct result in out, computed with the chosen plan.
-    return enqueue_fwd(h, best, c, stream);
+        for (const trimul::Plan& k2 : trimul::k2_choices()) {
+            if (e != hipSuccess) break;
+            trimul::Plan pl = best;
+            pl.k2_order = k2.k2_order;
+            pl.k2_gm = k2.k2_gm;
+            pl.k2_tile = k2.k2_tile;
+            double t;
+            time_best([&]() { return enq_project(h, pl, c, stream); }, [&]() { return enq_contract(h, pl, c, stream); },
+                      t);
+            if (e != hipSuccess) break;
+            if (t < best_k2) {
+                best_k2 = t;
+                best.k2_order = pl.k2_order;
+                best.k2_gm = pl.k2_gm;
+                best.k2_tile = pl.k2_tile;
+            }
+        }
+        const double best_ms = best_k1 + best_k2;
+        (void)hipEventDestroy(e0);
+        (void)hipEventDestroy(e1);
+        if (e != hipSuccess) return hip_fail("tuning run", e);
+        trimul::PlanEntry ent;
+        ent.key = key_of(c);
+        ent.plan = best;
+        ent.ms = best_ms;
+        set_plan(h, ent);
+        // The cache is best effort: a read-only or missing location only means the
+        // next process tunes again.
+        try {
+            (void)trimul::plan_cache_store(trimul::plan_cache_path(), h->arch, h->p.D, h->p.C, (int)h->p.dtype,
+                                           ent);
+        } catch (...) {
+        }
+        // Leave a correct result in out, computed with the chosen plan.
+        return enqueue_fwd(h, best, c, stream);
+    });
 }
 
 trimul_status trimul_internal_project(trimul_handle* h, const void* z, const void* pair_mask, int B,
@@ -784,92 +821,104 @@ trimul_status trimul_internal_output(trimul_handle* h, const void* z, const void
 trimul_status trimul_internal_set_plan(trimul_handle* h, int B, int N, trimul_direction dir, int masked,
                                        int k1_variant, int k2_order, int k2_gm, int k2_tile)
 {
-    if (!h) return fail(TRIMUL_ERR_INVALID_ARG, "handle is NULL");
-    trimul::PlanEntry ent;
-    ent.key = {B, N, enum_int(&dir), masked ? 1 : 0};
-    ent.plan.k1_variant = k1_variant;
-    ent.plan.k2_order = k2_order;
-    ent.plan.k2_gm = k2_gm;
-    ent.plan.k2_tile = k2_tile;
-    ent.ms = 0.0;
-    if (!trimul::plan_valid(ent.plan))
-        return fail(TRIMUL_ERR_INVALID_ARG, "no candidate plan has k1_variant=%d k2_order=%d k2_gm=%d k2_tile=%d",
-                    k1_variant, k2_order, k2_gm, k2_tile);
-    set_plan(h, ent);
-    return ok();
+    return guarded([&]() -> trimul_status {
+        if (!h) return fail(TRIMUL_ERR_INVALID_ARG, "handle is NULL");
+        trimul::PlanEntry ent;
+        ent.key = {B, N, enum_int(&dir), masked ? 1 : 0};
+        ent.plan.k1_variant = k1_variant;
+        ent.plan.k2_order = k2_order;
+        ent.plan.k2_gm = k2_gm;
+        ent.plan.k2_tile = k2_tile;
+        ent.ms = 0.0;
+        if (!trimul::plan_valid(ent.plan))
+            return fail(TRIMUL_ERR_INVALID_ARG, "no candidate plan has k1_variant=%d k2_order=%d k2_gm=%d k2_tile=%d",
+                        k1_variant, k2_order, k2_gm, k2_tile);
+        set_plan(h, ent);
+        return ok();
+    });
 }
 
 trimul_status trimul_internal_get_plan(trimul_handle* h, int B, int N, trimul_direction dir, int masked,
                                        int* k1_variant, int* k2_order, int* k2_gm, int* k2_tile)
 {
-    if (!h || !k1_variant || !k2_order || !k2_gm || !k2_tile)
-        return fail(TRIMUL_ERR_INVALID_ARG, "handle and outputs must be non-NULL");
-    const trimul::Plan p = plan_lookup(h, {B, N, enum_int(&dir), masked ? 1 : 0});
-    *k1_variant = p.k1_variant;
-    *k2_order = p.k2_order;
-    *k2_gm = p.k2_gm;
-    *k2_tile = p.k2_tile;
-    return ok();
+    return guarded([&]() -> trimul_status {
+        if (!h || !k1_variant || !k2_order || !k2_gm || !k2_tile)
+            return fail(TRIMUL_ERR_INVALID_ARG, "handle and outputs must be non-NULL");
+        const trimul::Plan p = plan_lookup(h, {B, N, enum_int(&dir), masked ? 1 : 0});
+        *k1_variant = p.k1_variant;
+        *k2_order = p.k2_order;
+        *k2_gm = p.k2_gm;
+        *k2_tile = p.k2_tile;
+        return ok();
+    });
 }
 
 int trimul_internal_plan_candidates(int* k1_variant, int* k2_order, int* k2_gm, int* k2_tile, int cap)
 {
-    const std::vector<trimul::Plan> c = trimul::candidate_plans();
-    for (int i = 0; i < (int)c.size() && i < cap; ++i) {
-        if (k1_variant) k1_variant[i] = c[i].k1_variant;
-        if (k2_order) k2_order[i] = c[i].k2_order;
-        if (k2_gm) k2_gm[i] = c[i].k2_gm;
-        if (k2_tile) k2_tile[i] = c[i].k2_tile;
-    }
-    return (int)c.size();
+    return guarded_int([&]() -> int {
+        const std::vector<trimul::Plan> c = trimul::candidate_plans();
+        for (int i = 0; i < (int)c.size() && i < cap; ++i) {
+            if (k1_variant) k1_variant[i] = c[i].k1_variant;
+            if (k2_order) k2_order[i] = c[i].k2_order;
+            if (k2_gm) k2_gm[i] = c[i].k2_gm;
+            if (k2_tile) k2_tile[i] = c[i].k2_tile;
+        }
+        return (int)c.size();
+    }, -1);
 }
 
 trimul_status trimul_internal_cache_store(const char* path, const char* device, int D, int C, int dtype,
                                           int B, int N, int dir, int masked, int k1_variant, int k2_order,
                                           int k2_gm, int k2_tile, double ms)
 {
-    if (!path || !device) return fail(TRIMUL_ERR_INVALID_ARG, "path and device must be non-NULL");
-    trimul::PlanEntry ent;
-    ent.key = {B, N, dir, masked};
-    ent.plan.k1_variant = k1_variant;
-    ent.plan.k2_order = k2_order;
-    ent.plan.k2_gm = k2_gm;
-    ent.plan.k2_tile = k2_tile;
-    ent.ms = ms;
-    if (!trimul::plan_valid(ent.plan))
-        return fail(TRIMUL_ERR_INVALID_ARG, "no candidate plan has k1_variant=%d k2_order=%d k2_gm=%d k2_tile=%d",
-                    k1_variant, k2_order, k2_gm, k2_tile);
-    if (!trimul::plan_cache_store(path, device, D, C, dtype, ent))
-        return fail(TRIMUL_ERR_INVALID_ARG, "could not write the plan cache %s", path);
-    return ok();
+    return guarded([&]() -> trimul_status {
+        if (!path || !device) return fail(TRIMUL_ERR_INVALID_ARG, "path and device must be non-NULL");
+        trimul::PlanEntry ent;
+        ent.key = {B, N, dir, masked};
+        ent.plan.k1_variant = k1_variant;
+        ent.plan.k2_order = k2_order;
+        ent.plan.k2_gm = k2_gm;
+        ent.plan.k2_tile = k2_tile;
+        ent.ms = ms;
+        if (!trimul::plan_valid(ent.plan))
+            return fail(TRIMUL_ERR_INVALID_ARG, "no candidate plan has k1_variant=%d k2_order=%d k2_gm=%d k2_tile=%d",
+                        k1_variant, k2_order, k2_gm, k2_tile);
+        if (!trimul::plan_cache_store(path, device, D, C, dtype, ent))
+            return fail(TRIMUL_ERR_INVALID_ARG, "could not write the plan cache %s", path);
+        return ok();
+    });
 }
 
 int trimul_internal_cache_lookup(const char* path, const char* device, int D, int C, int dtype, int B, int N,
                                  int dir, int masked, int* k1_variant, int* k2_order, int* k2_gm,
                                  int* k2_tile)
 {
-    if (!path || !device) return -1;
-    std::vector<trimul::PlanEntry> v;
-    if (!trimul::plan_cache_load(path, device, D, C, dtype, v)) return -1;
-    const trimul::PlanKey k = {B, N, dir, masked};
-    for (const trimul::PlanEntry& e : v)
-        if (e.key == k) {
-            if (k1_variant) *k1_variant = e.plan.k1_variant;
-            if (k2_order) *k2_order = e.plan.k2_order;
-            if (k2_gm) *k2_gm = e.plan.k2_gm;
-            if (k2_tile) *k2_tile = e.plan.k2_tile;
-            return 1;
-        }
-    return 0;
+    return guarded_int([&]() -> int {
+        if (!path || !device) return -1;
+        std::vector<trimul::PlanEntry> v;
+        if (!trimul::plan_cache_load(path, device, D, C, dtype, v)) return -1;
+        const trimul::PlanKey k = {B, N, dir, masked};
+        for (const trimul::PlanEntry& e : v)
+            if (e.key == k) {
+                if (k1_variant) *k1_variant = e.plan.k1_variant;
+                if (k2_order) *k2_order = e.plan.k2_order;
+                if (k2_gm) *k2_gm = e.plan.k2_gm;
+                if (k2_tile) *k2_tile = e.plan.k2_tile;
+                return 1;
+            }
+        return 0;
+    }, -1);
 }
 
 int trimul_internal_cache_path(char* buf, int cap)
 {
-    const std::string p = trimul::plan_cache_path();
-    if (buf && cap > 0) {
-        std::snprintf(buf, (size_t)cap, "%s", p.c_str());
-    }
-    return (int)p.size();
+    return guarded_int([&]() -> int {
+        const std::string p = trimul::plan_cache_path();
+        if (buf && cap > 0) {
+            std::snprintf(buf, (size_t)cap, "%s", p.c_str());
+        }
+        return (int)p.size();
+    }, 0);
 }
 
 }  // extern "C"
