@@ -295,7 +295,10 @@ class TriMul:
 
     ``forward(z, mask, direction)`` returns a new [B, N, N, D] tensor (or fills
     ``out``).  Tensors must be contiguous, on the device the handle was created
-    on, in the handle's dtype.
+    on, in the handle's dtype.  Calls through one TriMul object share its cached
+    workspace, so they must not overlap in time on different streams; for
+    concurrent calls, pass each its own workspace to ``trimul_fwd`` (the handle
+    itself is read-only after create).
     """
 
     # Device type every tensor argument must live on.
