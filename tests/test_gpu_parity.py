@@ -123,7 +123,8 @@ def test_project_stage(tb, dtype, direction, B, N, D, C):
 # ----------------------------------------------------------------------------
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("B,N,D,C", [(1, 24, 64, 64), (2, 40, 32, 96), (1, 16, 256, 256), (1, 8, 160, 224),
-                                     (1, 72, 128, 128), (2, 16, 128, 128), (2, 24, 256, 256)])
+                                     (1, 72, 128, 128), (2, 16, 128, 128), (2, 24, 256, 256),
+                                     (1, 24, 256, 128), (1, 40, 128, 256), (2, 24, 128, 64), (1, 16, 128, 192)])
 def test_output_stage(tb, dtype, B, N, D, C):
     say("output stage", dtype, B, N, D, C)
     w = inputs.make_weights(D, C, dtype, random_ln=True)
@@ -164,7 +165,9 @@ def test_output_stage_shifted_o_mean(tb, D, mean):
 @pytest.mark.parametrize("B,N,D,C,masked", [(1, 8, 32, 32, False), (3, 24, 64, 96, True),
                                             (1, 72, 128, 128, True), (2, 136, 32, 64, False),
                                             (1, 40, 256, 256, True), (1, 48, 160, 32, True),
-                                            (1, 24, 256, 192, True)])
+                                            (1, 24, 256, 192, True), (1, 40, 128, 256, True),
+                                            (2, 24, 256, 128, False), (1, 32, 128, 64, True),
+                                            (1, 136, 128, 192, False)])
 def test_fwd_small_shapes(tb, dtype, direction, B, N, D, C, masked):
     say("fwd small", dtype, direction, B, N, D, C, masked)
     w = inputs.make_weights(D, C, dtype, random_ln=True)

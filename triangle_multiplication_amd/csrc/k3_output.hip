@@ -312,6 +312,31 @@ template <> struct OFrags<4> {
         for (int k = 0; k < 4; ++k) y[k] = u32x4{r[2 * k][0], r[2 * k][1], r[2 * k + 1][0], r[2 * k + 1][1]};
     }
 };
+template <> struct OFrags<6> {
+    __device__ static inline void read(uint32_t a, u32x4 (&y)[6]) {
+        u32x2 r[12];
+        asm volatile(TRIMUL_TR2(0, 0) TRIMUL_TR2(1, 256) TRIMUL_TR2(2, 2048) TRIMUL_TR2(3, 2304)
+                     TRIMUL_TR2(4, 4096) TRIMUL_TR2(5, 4352) TRIMUL_TR2(6, 6144) TRIMUL_TR2(7, 6400)
+                     TRIMUL_TR2(8, 8192) TRIMUL_TR2(9, 8448) TRIMUL_TR2(10, 10240) TRIMUL_TR2(11, 10496)
+                     "s_waitcnt lgkmcnt(0)"
+                     : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
+                       "=&v"(r[6]), "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11])
+                     : [a] "v"(a));
+#pragma unroll
+        for (int k = 0; k < 6; ++k) y[k] = u32x4{r[2 * k][0], r[2 * k][1], r[2 * k + 1][0], r[2 * k + 1][1]};
+    }
+};
+template <> struct OFrags<2> {
+    __device__ static inline void read(uint32_t a, u32x4 (&y)[2]) {
+        u32x2 r[4];
+        asm volatile(TRIMUL_TR2(0, 0) TRIMUL_TR2(1, 256) TRIMUL_TR2(2, 2048) TRIMUL_TR2(3, 2304)
+                     "s_waitcnt lgkmcnt(0)"
+                     : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+                     : [a] "v"(a));
+#pragma unroll
+        for (int k = 0; k < 2; ++k) y[k] = u32x4{r[2 * k][0], r[2 * k][1], r[2 * k + 1][0], r[2 * k + 1][1]};
+    }
+};
 #undef TRIMUL_TR2
 
 template <int D, int C>
@@ -572,7 +597,10 @@ static hipError_t launch_k3_fold(const Params& p, const void* z, const OutputSrc
     if (hipGetDevice(&dev) == hipSuccess)
         (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     constexpr int NW = k3f::Cfg<D, C>::NW;
-    const long long slots = (long long)cus * (8 / NW);       // workgroups resident at once
+    // Workgroups resident per CU: 8 waves' worth, as far as the LDS ring allows.
+    constexpr int per_cu = (8 / NW) < (160 * 1024) / k3f::Cfg<D, C>::LDS ? (8 / NW) : (160 * 1024) / k3f::Cfg<D, C>::LDS;
+    static_assert(per_cu >= 1, "LDS");
+    const long long slots = (long long)cus * per_cu;          // workgroups resident at once
     const long long grid = n_super < slots ? n_super : slots;
     hipLaunchKernelGGL((k3_output_fold<D, C>), dim3((unsigned)grid), dim3(NW * 64), 0, s, (const bf16*)z,
                        o, (const bf16*)p.w_gout_f, (const bf16*)p.w_pout_f,
@@ -608,8 +636,17 @@ hipError_t launch_output(const Params& p, const void* z, const OutputSrc& o, int
 {
     if (p.dtype == DType::BF16 && p.D == 256 && p.C == 256)
         return launch_k3_fold<256, 256>(p, z, o, B, N, out, s);
-    if (p.dtype == DType::BF16 && p.D == 128 && p.C == 128)
-        return launch_k3_fold<128, 128>(p, z, o, B, N, out, s);
+    if (p.dtype == DType::BF16 && p.D == 256 && p.C == 128)
+        return launch_k3_fold<256, 128>(p, z, o, B, N, out, s);
+    if (p.dtype == DType::BF16 && p.D == 128) {
+        switch (p.C) {
+        case 64: return launch_k3_fold<128, 64>(p, z, o, B, N, out, s);
+        case 128: return launch_k3_fold<128, 128>(p, z, o, B, N, out, s);
+        case 192: return launch_k3_fold<128, 192>(p, z, o, B, N, out, s);
+        case 256: return launch_k3_fold<128, 256>(p, z, o, B, N, out, s);
+        default: break;
+        }
+    }
     if (p.dtype == DType::BF16) return launch_k3_d<bf16>(p, z, o, B, N, out, s);
     return launch_k3_d<float>(p, z, o, B, N, out, s);
 }
