@@ -245,7 +245,10 @@ struct K2PArgs {
     int order, gm;        // Plan
 };
 
-template <int NSP, int TB>
+// MK: the launch carries a mask table (args.ranges and the pair lists); the
+// unmasked instantiation runs every tile over all its K-steps with no table
+// reads and no per-tile range bookkeeping.
+template <int NSP, int TB, bool MK>
 __global__ __launch_bounds__(512) void k2_contract_ppp(K2PArgs args)
 {
     using namespace k2big;
@@ -272,7 +275,7 @@ __global__ __launch_bounds__(512) void k2_contract_ppp(K2PArgs args)
     const int nk = (N + BK * KH - 1) / (BK * KH);   // steps of a whole tile
     // Live-first pair lists exist for 256-row tiles only; 128-row tiles walk
     // the plain order and take the key range of the 256-row tiles holding them.
-    const bool use_pairs = TB == 256 && args.ranges;
+    constexpr bool use_pairs = TB == 256 && MK;
 
     // Tile tl of this workgroup: virtual block vb = g + tl*G through the
     // order's map, a bijection of [0, total) (total and G are multiples of 8),
@@ -318,15 +321,23 @@ __global__ __launch_bounds__(512) void k2_contract_ppp(K2PArgs args)
     // 32-key blocks of 256-row tiles; a step of KH blocks is run if any of its
     // blocks is live.
     const int t256 = (N + BM - 1) / BM;
+    // The values are uniform over the workgroup; readfirstlane keeps them in
+    // scalar registers, so the per-step cursor and loop tests stay scalar.
     auto krange = [&](size_t bc, int ti, int tj, int& klo, int& kn, bool& live) {
-        if (!args.ranges) { klo = 0; kn = nk; live = true; return; }
-        const int b = (int)(((size_t)args.bc0 + bc) / (size_t)args.C);
-        const int* r = args.ranges + (size_t)b * t256 * 2;
-        const int ui = ti * TB / BM, uj = tj * TB / BM;
-        const int lo = max(r[2 * ui], r[2 * uj]), hi = min(r[2 * ui + 1], r[2 * uj + 1]);
-        live = lo < hi;
-        klo = live ? lo / KH : 0;
-        kn = live ? (hi + KH - 1) / KH - lo / KH : 1;
+        if constexpr (!MK) {
+            klo = 0;
+            kn = nk;
+            live = true;
+        } else {
+            const int b = (int)(((size_t)args.bc0 + bc) / (size_t)args.C);
+            const int* r = args.ranges + (size_t)b * t256 * 2;
+            const int ui = ti * TB / BM, uj = tj * TB / BM;
+            const int lo = __builtin_amdgcn_readfirstlane(max(r[2 * ui], r[2 * uj]));
+            const int hi = __builtin_amdgcn_readfirstlane(min(r[2 * ui + 1], r[2 * uj + 1]));
+            live = lo < hi;
+            klo = live ? lo / KH : 0;
+            kn = live ? (hi + KH - 1) / KH - lo / KH : 1;
+        }
     };
 
     // Operand slab: [nk][N][32] bf16.  A slot holds, per operand, KH key
@@ -341,7 +352,7 @@ __global__ __launch_bounds__(512) void k2_contract_ppp(K2PArgs args)
     const int dr = 2 * (lane >> 3) + (dpos >> 2), dc = dpos & 3;
     constexpr unsigned qstride = 16u * ROWB;
     const unsigned kstride = (unsigned)N * ROWB;    // bytes per K-block
-    const int kh_w = (2 * wave) / RG;               // this wave's key block of a step
+    const int kh_w = KH == 1 ? 0 : __builtin_amdgcn_readfirstlane((2 * wave) / RG);   // its key block of a step
     const int g32 = ((2 * wave) % RG) / 2;          // its 32-row group of the tile
     const unsigned lane_off = (unsigned)(32 * g32 + dr) * ROWB + dc * 16u;
     // B rows are loaded permuted within each 32-row group: slot row 16 h + r
@@ -354,11 +365,13 @@ __global__ __launch_bounds__(512) void k2_contract_ppp(K2PArgs args)
     const unsigned lane_off_b = (unsigned)(32 * g32 + 8 * (dr >> 2) + (dr & 3)) * ROWB + dc * 16u;
 
     // DMA cursor: the next step to load is step ikk of tile itl (K-step
-    // iklo + ikk).  The tile's buffer descriptors, row offsets and K range are
+    // iklo + ikk; its first key ik0 and byte offset ikb advance by one step
+    // per issue).  The tile's buffer descriptors, row offsets and K range are
     // recomputed only when the cursor enters a new tile; past the workgroup's
     // last tile, in dead tiles and for K-chunks past N the offset is pushed
     // beyond the buffer's range, so the DMA reads zeros.
-    int itl = 0, ikk = 0, iklo = 0, ikn = 1;
+    int itl = 0, ikk = 0, iklo = 0, ikn = 1, ik0 = 0;
+    unsigned ikb = 0;
     __amdgpu_buffer_rsrc_t ra, rb;
     unsigned oa_t = 0, ob_t = 0;
     bool ilive = true;
@@ -374,15 +387,18 @@ __global__ __launch_bounds__(512) void k2_contract_ppp(K2PArgs args)
         rb = __builtin_amdgcn_make_buffer_rsrc((void*)(args.Bm + sb * aslab), 0, nrec, 0x00020000);
         oa_t = lane_off + (unsigned)(ti * TB) * ROWB;
         ob_t = lane_off_b + (unsigned)(tj * TB) * ROWB;
+        const int kk = iklo * KH + kh_w;                // key block of the tile's first step
+        ik0 = kk * BK;
+        ikb = (unsigned)kk * kstride;
     };
     set_tile();
     int isl = 0;                                    // ring slot of the next step
     auto issue = [&]() {
         unsigned char* st = smem + isl * STB + wave * DPO * 1024;
-        const int kk = (iklo + ikk) * KH + kh_w;     // key block
-        const int k0 = kk * BK;
-        const unsigned kb = (unsigned)kk * kstride;
-        const unsigned kpen = (ilive && k0 + dc * 8 < N) ? 0u : 0x80000000u;
+        const unsigned kb = ikb;
+        const unsigned kpen = (ilive && ik0 + dc * 8 < N) ? 0u : 0x80000000u;
+        ik0 += KH * BK;
+        ikb += (unsigned)KH * kstride;
 #pragma unroll
         for (int q = 0; q < DPO; ++q) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, TRIMUL_LDS_PTR(st + q * 1024), 16,
@@ -723,8 +739,14 @@ hipError_t launch_contract(const Params& p, const Plan& plan, const void* a_cm, 
         a.bc0 = job.bc0;
         a.order = plan.k2_order;
         a.gm = plan.k2_gm;
-        if (TB == 128) hipLaunchKernelGGL((k2_contract_ppp<4, 128>), dim3((unsigned)pg), dim3(512), 0, s, a);
-        else hipLaunchKernelGGL((k2_contract_ppp<4, 256>), dim3((unsigned)pg), dim3(512), 0, s, a);
+        const bool mk = job.table != nullptr;
+        if (TB == 128) {
+            if (mk) hipLaunchKernelGGL((k2_contract_ppp<4, 128, true>), dim3((unsigned)pg), dim3(512), 0, s, a);
+            else hipLaunchKernelGGL((k2_contract_ppp<4, 128, false>), dim3((unsigned)pg), dim3(512), 0, s, a);
+        } else {
+            if (mk) hipLaunchKernelGGL((k2_contract_ppp<4, 256, true>), dim3((unsigned)pg), dim3(512), 0, s, a);
+            else hipLaunchKernelGGL((k2_contract_ppp<4, 256, false>), dim3((unsigned)pg), dim3(512), 0, s, a);
+        }
         return hipGetLastError();
     }
     return launch_k2<float, 128, 128>(a_cm, b_cm, N, job, s);
