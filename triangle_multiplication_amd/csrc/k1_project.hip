@@ -232,7 +232,6 @@ __global__ __launch_bounds__(256) void k1_project(
 // ---------------------------------------------------------------------------
 namespace k1f {
 constexpr int RB = 4, ROWS = RB * 16, NWV = 4, NSW = 3, CMAX = 256;
-constexpr float LOG2E = 1.4426950408889634f;
 template <int D>
 struct Cfg {
     static constexpr int KG = D / 32;
@@ -247,10 +246,13 @@ struct Cfg {
 };
 }  // namespace k1f
 
-template <int D>
+// MK: a pair mask is given (every output is multiplied by its pair's mask
+// value, zero for pairs past N).  Without one, outputs of pairs past N are
+// not stored at all (their lanes write to the sink), so no multiply is needed.
+template <int D, bool MK>
 __global__ __launch_bounds__(256, 2) void k1_project_fold(
     const bf16* __restrict__ z, const bf16* __restrict__ mask, const bf16* __restrict__ Wf,
-    const bf16* __restrict__ Xf, float eps, bf16* __restrict__ a_cm, bf16* __restrict__ b_cm,
+    const float* __restrict__ Tv, float eps, bf16* __restrict__ a_cm, bf16* __restrict__ b_cm,
     bf16* __restrict__ sink, int N, int C, int incoming, int blocks_per_b)
 {
     using namespace k1f;
@@ -259,7 +261,7 @@ __global__ __launch_bounds__(256, 2) void k1_project_fold(
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     __shared__ __attribute__((aligned(1024))) unsigned char smem[Cf::LDS];
     unsigned char* ring = smem;
-    u32x4* ext = reinterpret_cast<u32x4*>(smem + NSW * STAGE);
+    f32x4* ext = reinterpret_cast<f32x4*>(smem + NSW * STAGE);
     float* sc = reinterpret_cast<float*>(smem + NSW * STAGE + Cf::EXT);
     // This wave's output tile of one stage: 16 channel rows of 64 pairs (128
     // bytes).  The 8-byte slot c of row r sits at c ^ (2 (r / 2)), so the
@@ -345,22 +347,22 @@ __global__ __launch_bounds__(256, 2) void k1_project_fold(
             zf[rb][kg] = live ? v : zero;
         }
     }
-    // Without a mask the load reads z (any valid address) and is discarded, so
-    // the load is not behind a branch either.
     float mval[RB];
-    const bf16* mb = mask ? mask + (size_t)bidx * NN : zb;
+    if constexpr (MK) {
+        const bf16* mb = mask + (size_t)bidx * NN;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        const int m = rb * 16 + l16;
-        const bool live = (m & 31) < kvalid;
-        const float mv = (float)mb[live ? zpair(m) : 0];
-        mval[rb] = live ? (mask ? mv : 1.0f) : 0.0f;
+        for (int rb = 0; rb < RB; ++rb) {
+            const int m = rb * 16 + l16;
+            const bool live = (m & 31) < kvalid;
+            const float mv = (float)mb[live ? zpair(m) : 0];
+            mval[rb] = live ? mv : 0.0f;
+        }
     }
     {
-        // Correction rows: 4C entries of 16 bytes, C/16 kilobytes.
+        // Accumulator start vectors: 4C entries of 16 bytes, C/16 kilobytes.
         const uint32_t lds_ext = lds_addr_of(ext);
         for (int q = wave_s; q < C / 16; q += NWV)
-            dma16_to_lds(Xf + (size_t)q * 512 + lane * 8, lds_ext + (uint32_t)(q * 1024));
+            dma16_to_lds(Tv + (size_t)q * 256 + lane * 4, lds_ext + (uint32_t)(q * 1024));
     }
     // Older than the DMA of stages 1 and 2, so the prologue's wait for stage 0
     // covers every load above.
@@ -398,7 +400,7 @@ __global__ __launch_bounds__(256, 2) void k1_project_fold(
                                   (__bf16)fmaf(__uint_as_float(w & 0xffff0000u), rstd, nmr)};
                 zf[rb][kg][h] = __builtin_bit_cast(uint32_t, x);
             }
-        if (g4 == 0) sc[(wave * RB + rb) * 16 + l16] = mval[rb];
+        if (MK && g4 == 0) sc[(wave * RB + rb) * 16 + l16] = mval[rb];
     }
     // Stage 0 landed (at most the DMA of stages 1 and 2 may be outstanding),
     // then publish it, the correction rows and the mask values.
@@ -428,27 +430,30 @@ __global__ __launch_bounds__(256, 2) void k1_project_fold(
     // Mask values of this lane's four output pairs in every block (they do not
     // change from stage to stage).
     f32x4 mrr[RB];
+    if constexpr (MK) {
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) mrr[rb] = *reinterpret_cast<const f32x4*>(sc + (wave * RB + rb) * 16 + 4 * g4);
-    // beta terms T = W beta of this lane's output channel (column l16 of stage
-    // q's 16 p rows and 16 g rows): T_h + T_l from the correction rows
-    // (S_h, S_l, S_h, T_h, T_l, T_h, 0, 0); the g term scaled by -log2(e).
-    auto tvals = [&](int q, float& tp, float& ntg) {
-        const u32x4 ep = ext[q * 32 + l16], eg = ext[q * 32 + 16 + l16];
-        const uint32_t p1 = ep[1], p2 = ep[2], g1 = eg[1], g2 = eg[2];
-        tp = __uint_as_float(p1 & 0xffff0000u) + __uint_as_float(p2 << 16);
-        ntg = -LOG2E * (__uint_as_float(g1 & 0xffff0000u) + __uint_as_float(g2 << 16));
+        for (int rb = 0; rb < RB; ++rb)
+            mrr[rb] = *reinterpret_cast<const f32x4*>(sc + (wave * RB + rb) * 16 + 4 * g4);
+    }
+    // Start vectors of this lane's output channel (column l16 of stage q's 16 p
+    // rows and 16 g rows): every accumulator of a stage starts at its channel's
+    // beta term, (T_p) x 4 and (-log2(e) T_g) x 4 (the gate rows of the folded
+    // weights carry the factor -log2(e) as well).
+    auto tvecs = [&](int q, f32x4& tp4, f32x4& tg4) {
+        tp4 = ext[q * 32 + l16];
+        tg4 = ext[q * 32 + 16 + l16];
     };
     auto fence = [&]() { __builtin_amdgcn_sched_barrier(0); };
     // One epilogue output (index k of NOUT) of the half Hp whose accumulators
-    // are pp/gp: a = m (acc_p + T_p) / (1 + 2^(-log2(e) (acc_g + T_g)));
-    // writes a block's four pairs to the output tile after its fourth output.
+    // are pp = p and gp = -log2(e) g: a = m p / (1 + 2^gp); writes a block's
+    // four pairs to the output tile after its fourth output.
     const int oswz = 2 * (l16 >> 1);
-    auto epi_out = [&](auto hpc, int k, const f32x4* pp, const f32x4* gp, f32x4* ov, float tp, float ntg) {
+    auto epi_out = [&](auto hpc, int k, const f32x4* pp, const f32x4* gp, f32x4* ov) {
         constexpr int HP = decltype(hpc)::value;
         const int j = k / 4, e = k % 4, rb = HP * HB + j;
-        ov[j][e] = mrr[rb][e] * (pp[j][e] + tp) *
-                   __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(fmaf(gp[j][e], -LOG2E, ntg)));
+        const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(gp[j][e]));
+        if constexpr (MK) ov[j][e] = mrr[rb][e] * pp[j][e] * sg;
+        else ov[j][e] = pp[j][e] * sg;
         if (e == 3) {
             bf16x4 h;
             h[0] = (bf16)ov[j][0]; h[1] = (bf16)ov[j][1]; h[2] = (bf16)ov[j][2]; h[3] = (bf16)ov[j][3];
@@ -476,17 +481,17 @@ __global__ __launch_bounds__(256, 2) void k1_project_fold(
             *reinterpret_cast<u32x4*>(p) = v;
         }
     };
-    // One half: MFMAs of blocks H of the stage in slot sl into ap/ag, starting
+    // One half: MFMAs of blocks H of stage qo (in slot sl) into ap/ag, starting
     // from the operands in b0/b1 (second half: prefetched by the first) and
     // leaving there the second half's (first half only).  If EPI, the previous
-    // half (HP, stage qp, accumulators pp/gp) is finished alongside.
+    // half (HP, accumulators pp/gp) is finished alongside.
     auto half = [&](auto hc, auto epic, auto hpc, const unsigned char* sl, u32x4& b0, u32x4& b1, f32x4* ap,
-                    f32x4* ag, int qp, const f32x4* pp, const f32x4* gp) {
+                    f32x4* ag, int qo, const f32x4* pp, const f32x4* gp) {
         constexpr int H = decltype(hc)::value;
         constexpr bool EPI = decltype(epic)::value;
         f32x4 ov[HB];
-        float tp = 0.f, ntg = 0.f;
-        if (EPI) tvals(qp, tp, ntg);
+        f32x4 tp4, tg4;
+        tvecs(qo, tp4, tg4);
         if (H == 0) {
             b0 = wfrag(sl, 0, 0);
             b1 = wfrag(sl, 1, 0);
@@ -507,9 +512,8 @@ __global__ __launch_bounds__(256, 2) void k1_project_fold(
             for (int j = 0; j < HB; ++j) {
                 const u32x4 a = zf[H * HB + j][st];
                 if (st == 0) {
-                    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
-                    ap[j] = Elem<bf16>::mma(a, b0, z4);
-                    ag[j] = Elem<bf16>::mma(a, b1, z4);
+                    ap[j] = Elem<bf16>::mma(a, b0, tp4);
+                    ag[j] = Elem<bf16>::mma(a, b1, tg4);
                 } else {
                     ap[j] = Elem<bf16>::mma(a, b0, ap[j]);
                     ag[j] = Elem<bf16>::mma(a, b1, ag[j]);
@@ -517,7 +521,7 @@ __global__ __launch_bounds__(256, 2) void k1_project_fold(
             }
             if (EPI) {
 #pragma unroll
-                for (int k = lo; k < hi; ++k) epi_out(hpc, k, pp, gp, ov, tp, ntg);
+                for (int k = lo; k < hi; ++k) epi_out(hpc, k, pp, gp, ov);
             }
             // Alternate MFMAs with the epilogue arithmetic inside the step.
             // The next step's LDS reads go after this step's first MFMA
@@ -549,7 +553,7 @@ __global__ __launch_bounds__(256, 2) void k1_project_fold(
     auto iteration = [&](auto sc, int q) -> bool {
         constexpr int S = decltype(sc)::value;
         const unsigned char* sl = ring + S * STAGE;
-        half(I1{}, T_{}, I0{}, sl, b0, b1, pB, gB, q, pA, gA);
+        half(I1{}, T_{}, I0{}, sl, b0, b1, pB, gB, q, pA, gA);   // second half of stage q
         if (q + 1 == NQ) return true;
         // Stage q + 1 must have landed.  Every wave issues, in this order per
         // iteration: the DMA of stage q + 3 (DPW instructions, while q + 3 <
@@ -563,7 +567,7 @@ __global__ __launch_bounds__(256, 2) void k1_project_fold(
         else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lds0(2));
         barrier();
         if (q + 3 < NQ) issue(q + 3, ring + S * STAGE);   // into the slot stage q used
-        half(I0{}, T_{}, I1{}, ring + ((S + 1) % NSW) * STAGE, b0, b1, pA, gA, q, pB, gB);
+        half(I0{}, T_{}, I1{}, ring + ((S + 1) % NSW) * STAGE, b0, b1, pA, gA, q + 1, pB, gB);
         store_tile(q);                   // the tile is complete; stage q + 1's epilogue starts after
         return false;
     };
@@ -574,10 +578,8 @@ __global__ __launch_bounds__(256, 2) void k1_project_fold(
     }
     {
         f32x4 ov[HB];
-        float tp, ntg;
-        tvals(NQ - 1, tp, ntg);
 #pragma unroll
-        for (int k = 0; k < NOUT; ++k) epi_out(I1{}, k, pB, gB, ov, tp, ntg);
+        for (int k = 0; k < NOUT; ++k) epi_out(I1{}, k, pB, gB, ov);
         store_tile(NQ - 1);
     }
 }
@@ -631,9 +633,14 @@ static hipError_t launch_k1_fold(const Params& p, const void* z, const void* mas
     const long long units = (long long)(N / 2) * ((N + 31) / 32);   // 64-pair units per batch element
     const int blocks_per_b = (int)((units + NWV - 1) / NWV);
     dim3 grid((unsigned)((size_t)B * blocks_per_b));
-    hipLaunchKernelGGL((k1_project_fold<D>), grid, dim3(256), 0, s, (const bf16*)z, (const bf16*)mask,
-                       (const bf16*)p.w_proj_f, (const bf16*)p.x_proj, p.eps, (bf16*)a, (bf16*)b,
-                       (bf16*)p.sink, N, p.C, incoming, blocks_per_b);
+    if (mask)
+        hipLaunchKernelGGL((k1_project_fold<D, true>), grid, dim3(256), 0, s, (const bf16*)z, (const bf16*)mask,
+                           (const bf16*)p.w_proj_f, (const float*)p.x_proj, p.eps, (bf16*)a, (bf16*)b,
+                           (bf16*)p.sink, N, p.C, incoming, blocks_per_b);
+    else
+        hipLaunchKernelGGL((k1_project_fold<D, false>), grid, dim3(256), 0, s, (const bf16*)z, nullptr,
+                           (const bf16*)p.w_proj_f, (const float*)p.x_proj, p.eps, (bf16*)a, (bf16*)b,
+                           (bf16*)p.sink, N, p.C, incoming, blocks_per_b);
     return hipGetLastError();
 }
 

@@ -136,6 +136,28 @@ void fold_rows(const float* W, const float* gamma, const float* beta, int rows, 
     }
 }
 
+// Folded projection for the bf16 projection kernel, rows in the kernel's order
+// (stages of 16 p rows then the same channels' 16 g rows).  Row r becomes
+// bf16(s W[r][k] gamma[k]) and gets the fp32 vector (T, T, T, T) with
+// T = s sum_k W[r][k] beta[k], where s = -log2(e) for gate rows and 1 for the
+// others: the kernel starts each accumulator at T, so a p accumulator ends at
+// p and a g accumulator at -log2(e) g, the exponent of the sigmoid's 2^x form.
+void fold_projection_rows(const float* W, const float* gamma, const float* beta, int rows, int K,
+                          uint16_t* wf, float* tv)
+{
+    const double log2e = 1.4426950408889634;
+    for (int r = 0; r < rows; ++r) {
+        const double sgn = (r % 32) >= 16 ? -log2e : 1.0;
+        double T = 0.0;
+        for (int k = 0; k < K; ++k) {
+            const double w = W[(size_t)r * K + k];
+            wf[(size_t)r * K + k] = f32_to_bf16((float)(sgn * w * gamma[k]));
+            T += w * beta[k];
+        }
+        for (int i = 0; i < 4; ++i) tv[(size_t)r * 4 + i] = (float)(sgn * T);
+    }
+}
+
 void put(std::vector<uint8_t>& dst, size_t off_elems, float v, trimul_dtype t)
 {
     if (t == TRIMUL_BF16) {
@@ -545,9 +567,9 @@ trimul_status trimul_create(int D, int C, trimul_dtype dtype_arg, const trimul_w
             std::vector<uint8_t> proj(n_proj * es);
             for (size_t i = 0; i < n_proj; ++i) put(proj, i, projf[i], dtype);
             if (folded)
-                fold_rows(projf.data(), w->norm_in_weight, w->norm_in_bias, 4 * C, D,
-                          reinterpret_cast<uint16_t*>(host.data() + off_wpf),
-                          reinterpret_cast<uint16_t*>(host.data() + off_xpj));
+                fold_projection_rows(projf.data(), w->norm_in_weight, w->norm_in_bias, 4 * C, D,
+                                     reinterpret_cast<uint16_t*>(host.data() + off_wpf),
+                                     reinterpret_cast<float*>(host.data() + off_xpj));
             for (size_t i = 0; i < n_go; ++i) put(go, i, w->g_out[i], dtype);
             for (size_t i = 0; i < n_po; ++i) put(po, i, w->p_out[i], dtype);
             std::memcpy(host.data() + off_proj, proj.data(), proj.size());

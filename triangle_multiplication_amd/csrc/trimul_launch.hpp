@@ -32,8 +32,9 @@ struct Params {
     // LayerNorm bias, each split into a bf16 high part and a bf16 remainder.
     const void* x_gout;
     const void* x_pout;
-    // The projection with ln_in_w folded in, rows in w_proj's order, and its
-    // [4C][8] correction rows (same form as x_gout).
+    // The projection with ln_in_w folded in, rows in w_proj's order with the
+    // gate rows scaled by -log2(e), and per row the fp32 vector (T, T, T, T) of
+    // its (equally scaled) dot product with ln_in_b: [4C][4] floats.
     const void* w_proj_f;
     const void* x_proj;
     // 4 KB of device memory that kernels with a fixed number of stores per
