@@ -481,26 +481,33 @@ __global__ __launch_bounds__(256, 2) void k1_project_fold(
             *reinterpret_cast<u32x4*>(p) = v;
         }
     };
-    // One half: MFMAs of blocks H of stage qo (in slot sl) into ap/ag, starting
-    // from the operands in b0/b1 (second half: prefetched by the first) and
-    // leaving there the second half's (first half only).  If EPI, the previous
-    // half (HP, accumulators pp/gp) is finished alongside.
-    auto half = [&](auto hc, auto epic, auto hpc, const unsigned char* sl, u32x4& b0, u32x4& b1, f32x4* ap,
+    // One half: MFMAs of blocks H of stage qo (in slot sl) into ap/ag.  The B
+    // operands (p and g weight fragments) are read two steps ahead: bq holds
+    // those of the half's first two steps (second half: prefetched by the
+    // first, which leaves them there).  If EPI, the previous half (HP,
+    // accumulators pp/gp) is finished alongside.
+    auto half = [&](auto hc, auto epic, auto hpc, const unsigned char* sl, u32x4 (&bq)[2][2], f32x4* ap,
                     f32x4* ag, int qo, const f32x4* pp, const f32x4* gp) {
         constexpr int H = decltype(hc)::value;
         constexpr bool EPI = decltype(epic)::value;
+        static_assert(KG >= 2, "two-step operand pipeline");
         f32x4 ov[HB];
         f32x4 tp4, tg4;
         tvecs(qo, tp4, tg4);
         if (H == 0) {
-            b0 = wfrag(sl, 0, 0);
-            b1 = wfrag(sl, 1, 0);
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                bq[s2][0] = wfrag(sl, 0, s2);
+                bq[s2][1] = wfrag(sl, 1, s2);
+            }
         }
+        u32x4 b0 = bq[0][0], b1 = bq[0][1], c0 = bq[1][0], c1 = bq[1][1];
 #pragma unroll
         for (int st = 0; st < KG; ++st) {
-            // Prefetch the next step's B operands (the second half's first).
-            const bool pre = st + 1 < KG || H == 0;
-            const int kn = st + 1 < KG ? st + 1 : 0;
+            // Prefetch the B operands of step st + 2 (past the end of the first
+            // half: the second half's first two steps, same slot).
+            const bool pre = st + 2 < KG || H == 0;
+            const int kn = st + 2 < KG ? st + 2 : st + 2 - KG;
             u32x4 n0, n1;
             if (pre) {
                 n0 = wfrag(sl, 0, kn);
@@ -534,7 +541,15 @@ __global__ __launch_bounds__(256, 2) void k1_project_fold(
                 __builtin_amdgcn_sched_group_barrier(0x0402, 3, 0);        // VALU / transcendental
             }
             fence();
-            if (pre) { b0 = n0; b1 = n1; }
+            b0 = c0;
+            b1 = c1;
+            if (pre) { c0 = n0; c1 = n1; }
+        }
+        if (H == 0) {
+            bq[0][0] = b0;
+            bq[0][1] = b1;
+            bq[1][0] = c0;
+            bq[1][1] = c1;
         }
     };
     using I0 = std::integral_constant<int, 0>;
@@ -542,8 +557,8 @@ __global__ __launch_bounds__(256, 2) void k1_project_fold(
     using T_ = std::integral_constant<bool, true>;
     using F_ = std::integral_constant<bool, false>;
     f32x4 pA[HB], gA[HB], pB[HB], gB[HB];
-    u32x4 b0, b1;
-    half(I0{}, F_{}, I1{}, ring, b0, b1, pA, gA, 0, pB, gB);
+    u32x4 bq[2][2];
+    half(I0{}, F_{}, I1{}, ring, bq, pA, gA, 0, pB, gB);
     // One iteration of the stage loop: the second half of stage q (ring slot
     // S = q % NSW) and the first half of stage q + 1.  S is a constant in each
     // of the NSW unrolled copies, so every LDS address of an iteration is a
@@ -553,7 +568,7 @@ __global__ __launch_bounds__(256, 2) void k1_project_fold(
     auto iteration = [&](auto sc, int q) -> bool {
         constexpr int S = decltype(sc)::value;
         const unsigned char* sl = ring + S * STAGE;
-        half(I1{}, T_{}, I0{}, sl, b0, b1, pB, gB, q, pA, gA);   // second half of stage q
+        half(I1{}, T_{}, I0{}, sl, bq, pB, gB, q, pA, gA);   // second half of stage q
         if (q + 1 == NQ) return true;
         // Stage q + 1 must have landed.  Every wave issues, in this order per
         // iteration: the DMA of stage q + 3 (DPW instructions, while q + 3 <
@@ -567,7 +582,7 @@ __global__ __launch_bounds__(256, 2) void k1_project_fold(
         else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lds0(2));
         barrier();
         if (q + 3 < NQ) issue(q + 3, ring + S * STAGE);   // into the slot stage q used
-        half(I0{}, T_{}, I1{}, ring + ((S + 1) % NSW) * STAGE, b0, b1, pA, gA, q + 1, pB, gB);
+        half(I0{}, T_{}, I1{}, ring + ((S + 1) % NSW) * STAGE, bq, pA, gA, q + 1, pB, gB);
         store_tile(q);                   // the tile is complete; stage q + 1's epilogue starts after
         return false;
     };
