@@ -160,6 +160,45 @@ def cpu_baseline(wl, z, mask, w, direction, n_sample):
     return res
 
 
+def measure_peaks(binding, torch, dev, reps=5):
+    """What the chip delivers to the simplest code on this machine: the bf16 rate
+    of an MFMA-only loop (two waves per SIMD, operands in registers, random
+    data) and the HBM rate of plain 16-byte streams with the kernels' read and
+    write mixes (1 GiB per buffer).  Best of `reps` timed launches each."""
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    g = torch.Generator(device="cpu").manual_seed(5)
+    seed = torch.randn(2048, generator=g).to(torch.bfloat16).to(dev)
+    blocks, iters = 2 * cus, 8192
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    mfma_flops = 4 * 16 * 16384 * iters * blocks
+    ms = _events_ms(lambda: binding.trimul_internal_peak_mfma(seed, blocks, iters, sink), 1)
+    ms = min(_events_ms(lambda: binding.trimul_internal_peak_mfma(seed, blocks, iters, sink), 1) for _ in range(reps))
+    mfma_tf = mfma_flops / (ms * 1e-3) / 1e12
+    n = 1 << 30
+    bufs = [torch.empty(n, dtype=torch.uint8, device=dev) for _ in range(4)]
+    for b in bufs[:2]:
+        b.fill_(7)
+    s0, s1, d0, d1 = bufs
+    rates = {}
+    for key, nbytes, kw in (("copy", 2 * n, {}), ("read2_write1", 3 * n, {"src1": s1}),
+                            ("read1_write2", 3 * n, {"dst1": d1})):
+        best = None
+        for nt in (False, True):
+            fn = lambda: binding.trimul_internal_peak_stream(s0, d0, nontemporal=nt, **kw)   # noqa: E731
+            _events_ms(fn, 1)
+            ms = min(_events_ms(fn, 1) for _ in range(reps))
+            best = ms if best is None else min(best, ms)
+        rates[key] = round(nbytes / best / 1e6, 1)
+    del bufs, s0, s1, d0, d1
+    torch.cuda.empty_cache()
+    return {"mfma_bf16_tflops": round(mfma_tf, 1), "stream_gbs": rates,
+            "method": ("MFMA-only loop: %d workgroups x 4 waves x %d iterations of 16 independent "
+                       "16x16x32 bf16 MFMAs on register operands; streams: one 16-byte chunk per thread over "
+                       "1 GiB buffers (copy: 1 read 1 write; read2_write1: the output stage's mix; "
+                       "read1_write2: the projection's), plain and non-temporal, the faster kept; best of %d "
+                       "launches, HIP events" % (blocks, iters, reps))}
+
+
 def executed_k2_flops(table, B, C, N, tile=256):
     """FLOPs the masked contraction executes: per tile pair, 2 * tile^2 *
     (8192 / tile) per live key step of 8192 / tile keys (dead tiles run one
@@ -202,6 +241,8 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=384,
                     help="side of the (i, j) grid the oracle computes for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-measured-peaks", action="store_true",
+                    help="skip the MFMA-only and stream kernels that measure this box's ceilings")
     ap.add_argument("--calibration-copy-gib", type=int, default=0,
                     help="only run one plain device copy of this many GiB (counter calibration) and exit")
     ap.add_argument("--print-k2-digest", action="store_true",
@@ -402,6 +443,18 @@ def main():
         "ms_per_step_wall": round(wall_ms, 4),
         "ms_per_step_events": round(ev_ms, 4),
     }
+    if not args.no_measured_peaks and wl.dtype == "bf16":
+        log("measured peaks ...")
+        mp = measure_peaks(binding, torch, dev)
+        result["measured_peaks"] = mp
+        sg = mp["stream_gbs"]
+        roof["measured_peak"] = mp["mfma_bf16_tflops"]
+        roof["frac_measured"] = round(k2_tf / mp["mfma_bf16_tflops"], 4)
+        kk = result["kernels"]
+        kk["k2_contract"]["mfma_frac_measured"] = roof["frac_measured"]
+        kk["k1_project"]["hbm_frac_measured"] = round(kk["k1_project"]["hbm_gbs"] / sg["read1_write2"], 4)
+        kk["k3_output"]["hbm_frac_measured"] = round(kk["k3_output"]["hbm_gbs"] / sg["read2_write1"], 4)
+        log("measured peaks: %s" % json.dumps(mp))
     if k0_ms is not None:
         result["kernels"]["k0_mask_ranges"] = {"ms": round(k0_ms, 4),
                                                "hbm_gbs": round(B * NN * es / k0_ms / 1e6, 1)}

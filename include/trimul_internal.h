@@ -105,6 +105,34 @@ int trimul_internal_cache_lookup(const char *path, const char *device, int D, in
                                  int *k2_gm, int *k2_tile);
 int trimul_internal_cache_path(char *buf, int cap);
 
+/*
+ * Measured ceilings for roofline figures (not part of the forward pass; the
+ * benchmark reports each kernel against these as well as against the spec
+ * peaks).  Both enqueue one kernel on `stream` and return at once.
+ *
+ * trimul_internal_peak_mfma: `blocks` workgroups of 256 threads (four waves);
+ * every wave loads bf16 operands once from `seed` (4096 bytes: 256 chunks of
+ * 16 bytes, 16-byte aligned) and then issues `iters` x 16 independent
+ * 16x16x32 bf16 MFMAs, 16384 FLOP each: 4 * 16 * 16384 * iters * blocks FLOP
+ * in all.  Thread t of workgroup g writes one float (a sum of its
+ * accumulators) to sink[g * 256 + t].  blocks in [1, 2^20], iters in
+ * [1, 2^24].
+ *
+ * trimul_internal_peak_stream: over n16 chunks of 16 bytes
+ * (1 <= n16 <= 2^38), one per thread, v = src0[i] (reads = 1) or
+ * src0[i] ^ src1[i] (reads = 2), then dst0[i] = v and, with writes = 2,
+ * dst1[i] = v: (reads + writes) * 16 * n16 bytes moved; nontemporal != 0
+ * marks every load and store non-temporal.
+ * Pointers the mode uses must be non-NULL and 16-byte aligned (unused ones
+ * may be NULL); (reads, writes) must be (1, 1), (2, 1) or (1, 2).
+ * Overlapping buffers give unspecified values but no access outside them.
+ */
+trimul_status trimul_internal_peak_mfma(const void *seed, int blocks, int iters, float *sink,
+                                        hipStream_t stream);
+trimul_status trimul_internal_peak_stream(const void *src0, const void *src1, void *dst0, void *dst1,
+                                          size_t n16, int reads, int writes, int nontemporal,
+                                          hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

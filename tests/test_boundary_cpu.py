@@ -210,3 +210,33 @@ def test_stage_helpers_check_shapes():
     with pytest.raises(ValueError) as e:
         layer.project(z, torch.zeros((1, 16, 8), dtype=torch.bfloat16))
     assert "mask" in str(e.value)
+
+
+def _vp(x):
+    return ctypes.c_void_p(x)
+
+
+@pytest.mark.parametrize("reads,writes", [(0, 1), (2, 2), (1, 0), (3, 1), (1, 3)])
+def test_peak_stream_rejects_unknown_modes(reads, writes):
+    st = tb._lib.trimul_internal_peak_stream(_vp(256), _vp(256), _vp(512), _vp(512), 4, reads, writes, 0, None)
+    assert st == tb.TRIMUL_ERR_INVALID_ARG
+    assert "(reads, writes)" in tb.trimul_last_error()
+
+
+def test_peak_stream_checks_pointers_and_size():
+    lib = tb._lib
+    assert lib.trimul_internal_peak_stream(None, None, _vp(512), None, 4, 1, 1, 0, None) == tb.TRIMUL_ERR_INVALID_ARG
+    assert lib.trimul_internal_peak_stream(_vp(256), None, _vp(512), None, 4, 2, 1, 0, None) == tb.TRIMUL_ERR_INVALID_ARG
+    assert lib.trimul_internal_peak_stream(_vp(256), None, _vp(512), None, 4, 1, 2, 0, None) == tb.TRIMUL_ERR_INVALID_ARG
+    assert lib.trimul_internal_peak_stream(_vp(256), None, _vp(520), None, 4, 1, 1, 0, None) == tb.TRIMUL_ERR_INVALID_ARG
+    assert "aligned" in tb.trimul_last_error()
+    assert lib.trimul_internal_peak_stream(_vp(256), None, _vp(512), None, 0, 1, 1, 0, None) == tb.TRIMUL_ERR_INVALID_ARG
+
+
+def test_peak_mfma_checks_arguments():
+    lib = tb._lib
+    assert lib.trimul_internal_peak_mfma(None, 1, 1, _vp(256), None) == tb.TRIMUL_ERR_INVALID_ARG
+    assert lib.trimul_internal_peak_mfma(_vp(256), 0, 1, _vp(256), None) == tb.TRIMUL_ERR_INVALID_ARG
+    assert lib.trimul_internal_peak_mfma(_vp(256), 1, 0, _vp(256), None) == tb.TRIMUL_ERR_INVALID_ARG
+    assert lib.trimul_internal_peak_mfma(_vp(264), 1, 1, _vp(256), None) == tb.TRIMUL_ERR_INVALID_ARG
+    assert "aligned" in tb.trimul_last_error()

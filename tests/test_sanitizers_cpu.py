@@ -37,7 +37,8 @@ def test_library_host_code_under_asan_ubsan(tmp_path):
         pytest.skip("hipcc not available")
     csrc = os.path.join(ROOT, "triangle_multiplication_amd", "csrc")
     inc = ["-I", os.path.join(ROOT, "include"), "-I", csrc]
-    srcs = ["trimul.cpp", "trimul_plans.cpp", "k1_project.hip", "k2_contract.hip", "k3_output.hip"]
+    from triangle_multiplication_amd import build as lib_build
+    srcs = list(lib_build.SOURCES)   # every source of libtrimul
 
     def build(src):
         obj = str(tmp_path / (src + ".o"))

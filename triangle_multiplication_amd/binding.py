@@ -38,7 +38,8 @@ EXPORTED = ["trimul_create", "trimul_destroy", "trimul_workspace_size", "trimul_
             "trimul_internal_project", "trimul_internal_mask_ranges", "trimul_internal_contract",
             "trimul_internal_output", "trimul_internal_set_plan", "trimul_internal_get_plan",
             "trimul_internal_plan_candidates", "trimul_internal_cache_store",
-            "trimul_internal_cache_lookup", "trimul_internal_cache_path"]
+            "trimul_internal_cache_lookup", "trimul_internal_cache_path",
+            "trimul_internal_peak_mfma", "trimul_internal_peak_stream"]
 
 
 class trimul_weights(ctypes.Structure):
@@ -92,6 +93,10 @@ _lib.trimul_internal_cache_lookup.argtypes = [ctypes.c_char_p, ctypes.c_char_p] 
 _lib.trimul_internal_cache_lookup.restype = _ci
 _lib.trimul_internal_cache_path.argtypes = [ctypes.c_char_p, _ci]
 _lib.trimul_internal_cache_path.restype = _ci
+_lib.trimul_internal_peak_mfma.argtypes = [_vp, _ci, _ci, _vp, _vp]
+_lib.trimul_internal_peak_mfma.restype = _ci
+_lib.trimul_internal_peak_stream.argtypes = [_vp, _vp, _vp, _vp, _sz, _ci, _ci, _ci, _vp]
+_lib.trimul_internal_peak_stream.restype = _ci
 
 
 class TriMulError(RuntimeError):
@@ -288,6 +293,30 @@ def trimul_internal_contract(h, a_cm, b_cm, o, table=None, direction="outgoing",
 def trimul_internal_output(h, z, o, out, stream=None):
     B, N = int(z.shape[0]), int(z.shape[1])
     _check(_lib.trimul_internal_output(h, _ptr(z), _ptr(o), B, N, _ptr(out), _stream(stream)))
+
+
+def trimul_internal_peak_mfma(seed, blocks, iters, sink, stream=None):
+    """MFMA-only loop: seed is 4096 bytes of bf16 operands, sink a float32
+    tensor of at least blocks * 256 elements; 4 * 16 * 16384 * iters * blocks FLOP."""
+    if seed.numel() * seed.element_size() < 4096:
+        raise ValueError("seed must hold 4096 bytes")
+    if sink.dtype.itemsize != 4 or sink.numel() < blocks * 256:
+        raise ValueError("sink must hold blocks * 256 float32 values")
+    _check(_lib.trimul_internal_peak_mfma(_ptr(seed), int(blocks), int(iters), _ptr(sink), _stream(stream)))
+
+
+def trimul_internal_peak_stream(src0, dst0, src1=None, dst1=None, nontemporal=False, stream=None):
+    """Stream 16-byte chunks: dst0 (and dst1) = src0 (xor src1); all given
+    tensors must have the byte size of src0, a multiple of 16."""
+    nbytes = src0.numel() * src0.element_size()
+    for t in (dst0, src1, dst1):
+        if t is not None and t.numel() * t.element_size() != nbytes:
+            raise ValueError("stream buffers must have equal byte sizes")
+    if nbytes % 16:
+        raise ValueError("stream buffers must be a multiple of 16 bytes")
+    _check(_lib.trimul_internal_peak_stream(_ptr(src0), _ptr(src1), _ptr(dst0), _ptr(dst1), nbytes // 16,
+                                            2 if src1 is not None else 1, 2 if dst1 is not None else 1,
+                                            1 if nontemporal else 0, _stream(stream)))
 
 
 class TriMul:

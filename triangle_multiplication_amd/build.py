@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libtrimul.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["trimul.cpp", "trimul_plans.cpp", "k1_project.hip", "k2_contract.hip", "k3_output.hip"]
+SOURCES = ["trimul.cpp", "trimul_plans.cpp", "k1_project.hip", "k2_contract.hip", "k3_output.hip", "peaks.hip"]
 
 COMMON = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -384,7 +384,9 @@ __global__ __launch_bounds__(k3f::waves_for(D) * 64) void k3_output_fold(
 
     // DMA of tile it into ring slot it % NS.  Instruction q covers 1 KB of the
     // slot; lane l fills its 16 bytes.  Phantom tiles (past the end) re-read
-    // tile 0 so that every wave issues the same count.
+    // tile 0 so that every wave issues the same count.  z is read with the
+    // non-temporal hint (each row is read once); o is not, since the second
+    // half of each of its 128-byte lines is read by the next tile from L2.
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);
     const uint32_t lds_ring = lds_addr_of(ring);
     auto issue = [&](int it) {
@@ -400,7 +402,7 @@ __global__ __launch_bounds__(k3f::waves_for(D) * 64) void k3_output_fold(
                 const int byte = q * 1024 + ln * 16;
                 const int row = byte / (D * 2), pch = (byte % (D * 2)) / 16;
                 const bf16* src = z + (p0 + row) * D + (pch ^ (row & 15)) * 8;
-                dma16_to_lds(src, sl + (uint32_t)(q * 1024));
+                dma16_to_lds_nt(src, sl + (uint32_t)(q * 1024));
             } else {
                 const int qo = q - Cf::ZDMA;
                 const int c = qo * 16 + (ln >> 2), pc = ln & 3;

@@ -840,6 +840,34 @@ trimul_status trimul_internal_output(trimul_handle* h, const void* z, const void
     return ok();
 }
 
+trimul_status trimul_internal_peak_mfma(const void* seed, int blocks, int iters, float* sink, hipStream_t stream)
+{
+    if (!seed || !sink) return fail(TRIMUL_ERR_INVALID_ARG, "seed and sink must be non-NULL");
+    if (!aligned(seed, 16) || !aligned(sink, 4))
+        return fail(TRIMUL_ERR_INVALID_ARG, "seed must be 16-byte aligned and sink 4-byte aligned");
+    if (blocks < 1 || blocks > (1 << 20)) return fail(TRIMUL_ERR_INVALID_ARG, "blocks must be in [1, 2^20]; got %d", blocks);
+    if (iters < 1 || iters > (1 << 24)) return fail(TRIMUL_ERR_INVALID_ARG, "iters must be in [1, 2^24]; got %d", iters);
+    hipError_t e = trimul::launch_peak_mfma(seed, blocks, iters, sink, stream);
+    if (e != hipSuccess) return hip_fail("MFMA peak kernel launch", e);
+    return ok();
+}
+
+trimul_status trimul_internal_peak_stream(const void* src0, const void* src1, void* dst0, void* dst1, size_t n16,
+                                          int reads, int writes, int nontemporal, hipStream_t stream)
+{
+    if (!((reads == 1 && writes == 1) || (reads == 2 && writes == 1) || (reads == 1 && writes == 2)))
+        return fail(TRIMUL_ERR_INVALID_ARG, "(reads, writes) must be (1, 1), (2, 1) or (1, 2); got (%d, %d)", reads, writes);
+    if (n16 < 1 || n16 > ((size_t)1 << 38)) return fail(TRIMUL_ERR_INVALID_ARG, "n16 must be in [1, 2^38]");
+    if (!src0 || !dst0 || (reads == 2 && !src1) || (writes == 2 && !dst1))
+        return fail(TRIMUL_ERR_INVALID_ARG, "a buffer the mode uses is NULL");
+    if (!aligned(src0, 16) || !aligned(dst0, 16) || (reads == 2 && !aligned(src1, 16)) ||
+        (writes == 2 && !aligned(dst1, 16)))
+        return fail(TRIMUL_ERR_INVALID_ARG, "stream buffers must be 16-byte aligned");
+    hipError_t e = trimul::launch_peak_stream(src0, src1, dst0, dst1, n16, reads, writes, nontemporal, stream);
+    if (e != hipSuccess) return hip_fail("stream peak kernel launch", e);
+    return ok();
+}
+
 trimul_status trimul_internal_set_plan(trimul_handle* h, int B, int N, trimul_direction dir, int masked,
                                        int k1_variant, int k2_order, int k2_gm, int k2_tile)
 {

@@ -129,6 +129,13 @@ __device__ inline void dma16_to_lds(const void* gaddr, uint32_t lds_addr)
     asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gaddr), "{m0}"(lds_addr) : "memory");
 }
 
+// The same with the non-temporal hint, for data a kernel reads exactly once
+// (it is then not kept in L2 at the expense of data that is re-read).
+__device__ inline void dma16_to_lds_nt(const void* gaddr, uint32_t lds_addr)
+{
+    asm volatile("global_load_lds_dwordx4 %0, off nt" ::"v"(gaddr), "{m0}"(lds_addr) : "memory");
+}
+
 // LDS byte address of a pointer into a __shared__ array.
 __device__ inline uint32_t lds_addr_of(const void* p)
 {
