@@ -477,7 +477,7 @@ __global__ __launch_bounds__(256, 2) void k1_project_fold(
             const int r = orow + 8 * i;
             const u32x4 v = *reinterpret_cast<const u32x4*>(otile + r * 128 + (((2 * ochk) ^ (2 * (r >> 1))) << 3));
             bf16* p = (full || olive) ? base + (size_t)r * slab_ab : sink + lane * 8;
-            *reinterpret_cast<u32x4*>(p) = v;
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));   // streamed out, read back by K2 from HBM
         }
     };
     // One half: MFMAs of blocks H of stage qo (in slot sl) into ap/ag.  The B
