@@ -231,9 +231,9 @@ __global__ __launch_bounds__(256) void k3_output(
 // The epilogue is then out = (rstd_o acc_p) / (1 + 2^(-log2(e) rstd_x acc_g)).
 //
 // Persistent workgroups (one of 8 waves per CU at D = 256, two of 4 waves at
-// D = 128) walk 32-pair tiles; the two halves of each 64-pair run go to the
-// same workgroup back to back, so the second half of every 128-byte line of o
-// is an L2 hit.  Each wave owns two 16-row blocks of the D output channels
+// D = 128) walk 32-pair tiles of a contiguous range of pairs; the two halves
+// of each 64-pair run go to the same workgroup back to back, so the second
+// half of every 128-byte line of o is an L2 hit.  Each wave owns two 16-row blocks of the D output channels
 // (rows interleaved so that a lane's results are eight consecutive channels)
 // and holds those rows of W'_g and W'_p in registers for the whole kernel.  A ring of four LDS slots, filled by
 // global->LDS DMA three tiles ahead, holds per tile
@@ -358,10 +358,14 @@ __global__ __launch_bounds__(k3f::waves_for(D) * 64) void k3_output_fold(
     const int l16 = lane & 15, g4 = lane >> 4;
     const size_t NN = (size_t)N * N;
     const int G = gridDim.x, g = blockIdx.x;
-    // This workgroup's tiles: 64-pair runs g, g + G, ..., each as two 32-pair halves.
-    const int n_tiles = 2 * ((n_super - g + G - 1) / G);
+    // This workgroup's tiles: one contiguous range of 64-pair runs, each as two
+    // 32-pair halves, so every workgroup streams its own contiguous stretch of
+    // z, out and each channel of o (measured against walking runs g, g + G,
+    // ...: -1 % at D = 256, -7 % at D = 128 with two workgroups per CU).
+    const long long s_begin = (long long)g * n_super / G, s_end = (long long)(g + 1) * n_super / G;
+    const int n_tiles = 2 * (int)(s_end - s_begin);
     auto tile_p0 = [&](int it) -> size_t {
-        return it < n_tiles ? ((size_t)(g + (it >> 1) * G) * 64 + (it & 1) * 32) : 0;
+        return it < n_tiles ? ((size_t)(s_begin + (it >> 1)) * 64 + (it & 1) * 32) : 0;
     };
 
     // Weight rows of this wave (MFMA A operand: lane = row l16 of the block,
