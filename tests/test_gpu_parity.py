@@ -118,6 +118,27 @@ def test_project_stage(tb, dtype, direction, B, N, D, C):
         assert (a[:, :, :, dead] == 0).all() and (a[:, :, dead, :] == 0).all()
 
 
+@pytest.mark.parametrize("direction", ["outgoing", "incoming"])
+@pytest.mark.parametrize("B,N,D,C", [(1, 40, 128, 32), (2, 72, 128, 96), (1, 40, 256, 224), (1, 64, 256, 256),
+                                     (1, 24, 256, 128), (1, 40, 128, 256)])
+def test_project_stage_unmasked(tb, direction, B, N, D, C):
+    """The bf16 projection without a mask runs its own instantiation (no mask
+    loads or multiply; lanes of pairs past N store to the sink): a and b against
+    the oracle, ragged k blocks included."""
+    say("project stage unmasked", direction, B, N, D, C)
+    w = inputs.make_weights(D, C, "bf16", random_ln=True)
+    z = inputs.make_z(B, N, D, "bf16")
+    ref = oracle.trimul_full(z.float().numpy(), None, w, direction, dumps=True)
+    layer = _layer(tb, w, "bf16")
+    a, b = layer.project(z.cuda(), None, direction)
+    a, b = _from_ab_storage(a, "bf16"), _from_ab_storage(b, "bf16")
+    a, b = a.float().cpu().numpy(), b.float().cpu().numpy()
+    ra, rb = ref["a"], ref["b"]
+    perm = (0, 3, 1, 2) if direction == "outgoing" else (0, 3, 2, 1)
+    assert rel_err(a, ra.transpose(perm)) <= TOL["bf16"]
+    assert rel_err(b, rb.transpose(perm)) <= TOL["bf16"]
+
+
 # ----------------------------------------------------------------------------
 # Output kernel alone against the oracle's output stage
 # ----------------------------------------------------------------------------
@@ -137,14 +158,15 @@ def test_output_stage(tb, dtype, B, N, D, C):
     assert rel_err(out.float().cpu().numpy(), ref) <= TOL[dtype]
 
 
-@pytest.mark.parametrize("D", [128, 256])
+@pytest.mark.parametrize("D,C", [(128, 128), (256, 256), (256, 128), (128, 256), (128, 64), (128, 192)])
 @pytest.mark.parametrize("mean", [20.0, -40.0])
-def test_output_stage_shifted_o_mean(tb, D, mean):
-    """o channels far from zero mean (sigma 1): the folded output kernel takes
-    LayerNorm_out's statistics in one pass and applies -mu * S algebraically on
-    bf16-stored o, so the cancellation must stay within tolerance."""
-    B, N, C = 1, 40, D
-    say("output stage shifted o mean", D, mean)
+def test_output_stage_shifted_o_mean(tb, D, C, mean):
+    """o channels far from zero mean (sigma 1): the folded output kernel (every
+    width it serves) takes LayerNorm_out's statistics in one pass and applies
+    -mu * S algebraically on bf16-stored o, so the cancellation must stay
+    within tolerance."""
+    B, N = 1, 40
+    say("output stage shifted o mean", D, C, mean)
     w = inputs.make_weights(D, C, "bf16", random_ln=True)
     z = inputs.make_z(B, N, D, "bf16")
     g = torch.Generator("cpu").manual_seed(10)
