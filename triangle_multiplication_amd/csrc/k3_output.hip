@@ -361,11 +361,20 @@ __global__ __launch_bounds__(k3f::waves_for(D) * 64) void k3_output_fold(
     // This workgroup's tiles: one contiguous range of 64-pair runs, each as two
     // 32-pair halves, so every workgroup streams its own contiguous stretch of
     // z, out and each channel of o (measured against walking runs g, g + G,
-    // ...: -1 % at D = 256, -7 % at D = 128 with two workgroups per CU).
+    // ...: -1 % at D = 256, -7 % at D = 128 with two workgroups per CU).  The
+    // walk starts at a position rotated by 97 g runs within the range and
+    // wraps: with aligned starts, the lines the workgroups of an XCD read at
+    // the same time sat at power-of-two distances and evicted each other from
+    // L2, so a third of o's lines were fetched twice (the next tile reads the
+    // second half of each).
     const long long s_begin = (long long)g * n_super / G, s_end = (long long)(g + 1) * n_super / G;
-    const int n_tiles = 2 * (int)(s_end - s_begin);
+    const int n_runs = (int)(s_end - s_begin);
+    const int n_tiles = 2 * n_runs;
+    const int rot = n_runs > 0 ? (int)(((long long)g * 97) % n_runs) : 0;
     auto tile_p0 = [&](int it) -> size_t {
-        return it < n_tiles ? ((size_t)(s_begin + (it >> 1)) * 64 + (it & 1) * 32) : 0;
+        int r = (it >> 1) + rot;
+        if (r >= n_runs) r -= n_runs;
+        return it < n_tiles ? ((size_t)(s_begin + r) * 64 + (it & 1) * 32) : 0;
     };
 
     // Weight rows of this wave (MFMA A operand: lane = row l16 of the block,
