@@ -170,10 +170,16 @@ def measure_peaks(binding, torch, dev, reps=5):
     seed = torch.randn(2048, generator=g).to(torch.bfloat16).to(dev)
     blocks, iters = 2 * cus, 8192
     sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
-    mfma_flops = 4 * 16 * 16384 * iters * blocks
-    ms = _events_ms(lambda: binding.trimul_internal_peak_mfma(seed, blocks, iters, sink), 1)
-    ms = min(_events_ms(lambda: binding.trimul_internal_peak_mfma(seed, blocks, iters, sink), 1) for _ in range(reps))
-    mfma_tf = mfma_flops / (ms * 1e-3) / 1e12
+    mfma_flops = 4 * 262144 * iters * blocks
+    shape_tf = {}
+    for _ in range(2):          # warm both shapes up first (the clock ramps over the first launches)
+        for shape in (0, 1):
+            _events_ms(lambda: binding.trimul_internal_peak_mfma(seed, blocks, iters, sink, shape=shape), 1)
+    for shape, key in ((0, "16x16x32"), (1, "32x32x16")):
+        ms = min(_events_ms(lambda: binding.trimul_internal_peak_mfma(seed, blocks, iters, sink, shape=shape), 1)
+                 for _ in range(reps))
+        shape_tf[key] = round(mfma_flops / (ms * 1e-3) / 1e12, 1)
+    mfma_tf = max(shape_tf.values())
     n = 1 << 30
     bufs = [torch.empty(n, dtype=torch.uint8, device=dev) for _ in range(4)]
     for b in bufs[:2]:
@@ -191,9 +197,9 @@ def measure_peaks(binding, torch, dev, reps=5):
         rates[key] = round(nbytes / best / 1e6, 1)
     del bufs, s0, s1, d0, d1
     torch.cuda.empty_cache()
-    return {"mfma_bf16_tflops": round(mfma_tf, 1), "stream_gbs": rates,
+    return {"mfma_bf16_tflops": round(mfma_tf, 1), "mfma_bf16_tflops_by_shape": shape_tf, "stream_gbs": rates,
             "method": ("MFMA-only loop: %d workgroups x 4 waves x %d iterations of 16 independent "
-                       "16x16x32 bf16 MFMAs on register operands; streams: one 16-byte chunk per thread over "
+                       "16x16x32 (or 8 32x32x16) bf16 MFMAs on register operands, the faster shape kept; streams: one 16-byte chunk per thread over "
                        "1 GiB buffers (copy: 1 read 1 write; read2_write1: the output stage's mix; "
                        "read1_write2: the projection's), plain and non-temporal, the faster kept; best of %d "
                        "launches, HIP events" % (blocks, iters, reps))}

@@ -112,11 +112,12 @@ int trimul_internal_cache_path(char *buf, int cap);
  *
  * trimul_internal_peak_mfma: `blocks` workgroups of 256 threads (four waves);
  * every wave loads bf16 operands once from `seed` (4096 bytes: 256 chunks of
- * 16 bytes, 16-byte aligned) and then issues `iters` x 16 independent
- * 16x16x32 bf16 MFMAs, 16384 FLOP each: 4 * 16 * 16384 * iters * blocks FLOP
+ * 16 bytes, 16-byte aligned) and then issues, per iteration, 16 independent
+ * 16x16x32 bf16 MFMAs (shape 0) or 8 32x32x16 bf16 MFMAs on 4 accumulator
+ * tiles (shape 1), 262144 FLOP either way: 4 * 262144 * iters * blocks FLOP
  * in all.  Thread t of workgroup g writes one float (a sum of its
  * accumulators) to sink[g * 256 + t].  blocks in [1, 2^20], iters in
- * [1, 2^24].
+ * [1, 2^24], shape 0 or 1.
  *
  * trimul_internal_peak_stream: over n16 chunks of 16 bytes
  * (1 <= n16 <= 2^38), one per thread, v = src0[i] (reads = 1) or
@@ -127,7 +128,7 @@ int trimul_internal_cache_path(char *buf, int cap);
  * may be NULL); (reads, writes) must be (1, 1), (2, 1) or (1, 2).
  * Overlapping buffers give unspecified values but no access outside them.
  */
-trimul_status trimul_internal_peak_mfma(const void *seed, int blocks, int iters, float *sink,
+trimul_status trimul_internal_peak_mfma(const void *seed, int blocks, int iters, int shape, float *sink,
                                         hipStream_t stream);
 trimul_status trimul_internal_peak_stream(const void *src0, const void *src1, void *dst0, void *dst1,
                                           size_t n16, int reads, int writes, int nontemporal,

@@ -235,8 +235,10 @@ def test_peak_stream_checks_pointers_and_size():
 
 def test_peak_mfma_checks_arguments():
     lib = tb._lib
-    assert lib.trimul_internal_peak_mfma(None, 1, 1, _vp(256), None) == tb.TRIMUL_ERR_INVALID_ARG
-    assert lib.trimul_internal_peak_mfma(_vp(256), 0, 1, _vp(256), None) == tb.TRIMUL_ERR_INVALID_ARG
-    assert lib.trimul_internal_peak_mfma(_vp(256), 1, 0, _vp(256), None) == tb.TRIMUL_ERR_INVALID_ARG
-    assert lib.trimul_internal_peak_mfma(_vp(264), 1, 1, _vp(256), None) == tb.TRIMUL_ERR_INVALID_ARG
+    assert lib.trimul_internal_peak_mfma(None, 1, 1, 0, _vp(256), None) == tb.TRIMUL_ERR_INVALID_ARG
+    assert lib.trimul_internal_peak_mfma(_vp(256), 0, 1, 0, _vp(256), None) == tb.TRIMUL_ERR_INVALID_ARG
+    assert lib.trimul_internal_peak_mfma(_vp(256), 1, 0, 0, _vp(256), None) == tb.TRIMUL_ERR_INVALID_ARG
+    assert lib.trimul_internal_peak_mfma(_vp(256), 1, 1, 2, _vp(256), None) == tb.TRIMUL_ERR_INVALID_ARG
+    assert "shape" in tb.trimul_last_error()
+    assert lib.trimul_internal_peak_mfma(_vp(264), 1, 1, 0, _vp(256), None) == tb.TRIMUL_ERR_INVALID_ARG
     assert "aligned" in tb.trimul_last_error()

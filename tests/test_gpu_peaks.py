@@ -43,14 +43,15 @@ def test_streams_move_the_defined_bytes(tb, n16, nt):
     assert torch.equal(d0, s0) and torch.equal(d1, s0)
 
 
-def test_mfma_loop_accumulates_linearly(tb):
+@pytest.mark.parametrize("shape", [0, 1])
+def test_mfma_loop_accumulates_linearly(tb, shape):
     g = torch.Generator(device="cpu").manual_seed(5)
     seed = torch.randn(2048, generator=g).to(torch.bfloat16).cuda()
     blocks = 64
     one = torch.full((blocks * 256,), float("nan"), device="cuda")
     two = torch.full((blocks * 256,), float("nan"), device="cuda")
-    tb.trimul_internal_peak_mfma(seed, blocks, 1, one)
-    tb.trimul_internal_peak_mfma(seed, blocks, 2, two)
+    tb.trimul_internal_peak_mfma(seed, blocks, 1, one, shape=shape)
+    tb.trimul_internal_peak_mfma(seed, blocks, 2, two, shape=shape)
     torch.cuda.synchronize()
     assert torch.isfinite(one).all() and torch.isfinite(two).all()
     assert one.abs().max() > 0

@@ -93,7 +93,7 @@ _lib.trimul_internal_cache_lookup.argtypes = [ctypes.c_char_p, ctypes.c_char_p] 
 _lib.trimul_internal_cache_lookup.restype = _ci
 _lib.trimul_internal_cache_path.argtypes = [ctypes.c_char_p, _ci]
 _lib.trimul_internal_cache_path.restype = _ci
-_lib.trimul_internal_peak_mfma.argtypes = [_vp, _ci, _ci, _vp, _vp]
+_lib.trimul_internal_peak_mfma.argtypes = [_vp, _ci, _ci, _ci, _vp, _vp]
 _lib.trimul_internal_peak_mfma.restype = _ci
 _lib.trimul_internal_peak_stream.argtypes = [_vp, _vp, _vp, _vp, _sz, _ci, _ci, _ci, _vp]
 _lib.trimul_internal_peak_stream.restype = _ci
@@ -295,14 +295,16 @@ def trimul_internal_output(h, z, o, out, stream=None):
     _check(_lib.trimul_internal_output(h, _ptr(z), _ptr(o), B, N, _ptr(out), _stream(stream)))
 
 
-def trimul_internal_peak_mfma(seed, blocks, iters, sink, stream=None):
-    """MFMA-only loop: seed is 4096 bytes of bf16 operands, sink a float32
-    tensor of at least blocks * 256 elements; 4 * 16 * 16384 * iters * blocks FLOP."""
+def trimul_internal_peak_mfma(seed, blocks, iters, sink, shape=0, stream=None):
+    """MFMA-only loop (shape 0: 16x16x32, 1: 32x32x16 bf16 MFMAs): seed is 4096
+    bytes of bf16 operands, sink a float32 tensor of at least blocks * 256
+    elements; 4 * 262144 * iters * blocks FLOP."""
     if seed.numel() * seed.element_size() < 4096:
         raise ValueError("seed must hold 4096 bytes")
     if sink.dtype.itemsize != 4 or sink.numel() < blocks * 256:
         raise ValueError("sink must hold blocks * 256 float32 values")
-    _check(_lib.trimul_internal_peak_mfma(_ptr(seed), int(blocks), int(iters), _ptr(sink), _stream(stream)))
+    _check(_lib.trimul_internal_peak_mfma(_ptr(seed), int(blocks), int(iters), int(shape), _ptr(sink),
+                                          _stream(stream)))
 
 
 def trimul_internal_peak_stream(src0, dst0, src1=None, dst1=None, nontemporal=False, stream=None):

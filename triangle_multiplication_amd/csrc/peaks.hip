@@ -3,10 +3,13 @@
 // The spec peaks (2.5 PFLOP/s dense bf16, 8 TB/s HBM) assume the 2.4 GHz
 // clock and an ideal memory system.  These kernels measure what the chip
 // delivers to the simplest possible code on the same box:
-//  - peak_mfma_bf16: every wave issues nothing but independent
-//    v_mfma_f32_16x16x32_bf16 on operands held in registers (16 accumulator
-//    tiles per wave, two waves per SIMD as in the contraction), on random
-//    bf16 data, so the matrix cores toggle like they do on real operands;
+//  - peak_mfma_bf16<SHAPE>: every wave issues nothing but independent bf16
+//    MFMAs on operands held in registers (two waves per SIMD as in the
+//    contraction), on random bf16 data, so the matrix cores toggle like they
+//    do on real operands: 16 accumulator tiles of v_mfma_f32_16x16x32_bf16
+//    (SHAPE 0, the instruction the kernels use) or 4 tiles of
+//    v_mfma_f32_32x32x16_bf16 (SHAPE 1, measured about 3 % faster), the same
+//    registers and FLOPs per iteration;
 //  - peak_stream<R, W, NT>: one 16-byte chunk per thread over a grid that
 //    covers the arrays, R source arrays read and W destination arrays written
 //    per chunk (copy: 1/1; the output stage's mix: 2/1; the projection's
@@ -23,6 +26,9 @@ namespace trimul {
 
 constexpr int PEAK_THREADS = 256;
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+template <int SHAPE>
 __global__ __launch_bounds__(PEAK_THREADS) void peak_mfma_bf16(const u32x4* __restrict__ seed, int iters,
                                                                float* __restrict__ sink)
 {
@@ -34,18 +40,41 @@ __global__ __launch_bounds__(PEAK_THREADS) void peak_mfma_bf16(const u32x4* __re
         a[i] = seed[(lane + 64 * i + 16 * wave) & 255];
         b[i] = seed[(lane + 64 * i + 128 + 16 * wave) & 255];
     }
-    f32x4 acc[16];
-#pragma unroll
-    for (int t = 0; t < 16; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int it = 0; it < iters; ++it) {
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-            for (int n = 0; n < 4; ++n) acc[4 * m + n] = Elem<bf16>::mma(a[m], b[n], acc[4 * m + n]);
-    }
     float s = 0.f;
+    if constexpr (SHAPE == 0) {
+        f32x4 acc[16];
 #pragma unroll
-    for (int t = 0; t < 16; ++t) s += acc[t][0] + acc[t][1] + acc[t][2] + acc[t][3];
+        for (int t = 0; t < 16; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int it = 0; it < iters; ++it) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int n = 0; n < 4; ++n) acc[4 * m + n] = Elem<bf16>::mma(a[m], b[n], acc[4 * m + n]);
+        }
+#pragma unroll
+        for (int t = 0; t < 16; ++t) s += acc[t][0] + acc[t][1] + acc[t][2] + acc[t][3];
+    } else {
+        f32x16 acc[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[t][e] = 0.f;
+        for (int it = 0; it < iters; ++it) {
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int n = 0; n < 2; ++n) {
+                    acc[2 * m + n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8, a[m]), __builtin_bit_cast(bf16x8, b[n]), acc[2 * m + n], 0, 0, 0);
+                    acc[2 * m + n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8, a[m + 2]), __builtin_bit_cast(bf16x8, b[n + 2]), acc[2 * m + n], 0, 0, 0);
+                }
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) s += acc[t][e];
+    }
     sink[(size_t)blockIdx.x * PEAK_THREADS + threadIdx.x] = s;
 }
 
@@ -68,10 +97,16 @@ __global__ __launch_bounds__(PEAK_THREADS) void peak_stream(const u32x4* __restr
     }
 }
 
-hipError_t launch_peak_mfma(const void* seed, int blocks, int iters, float* sink, hipStream_t s)
+hipError_t launch_peak_mfma(const void* seed, int blocks, int iters, int shape, float* sink, hipStream_t s)
 {
-    hipLaunchKernelGGL(peak_mfma_bf16, dim3((unsigned)blocks), dim3(PEAK_THREADS), 0, s,
-                       (const u32x4*)seed, iters, sink);
+    if (shape == 0)
+        hipLaunchKernelGGL((peak_mfma_bf16<0>), dim3((unsigned)blocks), dim3(PEAK_THREADS), 0, s,
+                           (const u32x4*)seed, iters, sink);
+    else if (shape == 1)
+        hipLaunchKernelGGL((peak_mfma_bf16<1>), dim3((unsigned)blocks), dim3(PEAK_THREADS), 0, s,
+                           (const u32x4*)seed, iters, sink);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

@@ -840,14 +840,16 @@ trimul_status trimul_internal_output(trimul_handle* h, const void* z, const void
     return ok();
 }
 
-trimul_status trimul_internal_peak_mfma(const void* seed, int blocks, int iters, float* sink, hipStream_t stream)
+trimul_status trimul_internal_peak_mfma(const void* seed, int blocks, int iters, int shape, float* sink,
+                                        hipStream_t stream)
 {
     if (!seed || !sink) return fail(TRIMUL_ERR_INVALID_ARG, "seed and sink must be non-NULL");
     if (!aligned(seed, 16) || !aligned(sink, 4))
         return fail(TRIMUL_ERR_INVALID_ARG, "seed must be 16-byte aligned and sink 4-byte aligned");
     if (blocks < 1 || blocks > (1 << 20)) return fail(TRIMUL_ERR_INVALID_ARG, "blocks must be in [1, 2^20]; got %d", blocks);
     if (iters < 1 || iters > (1 << 24)) return fail(TRIMUL_ERR_INVALID_ARG, "iters must be in [1, 2^24]; got %d", iters);
-    hipError_t e = trimul::launch_peak_mfma(seed, blocks, iters, sink, stream);
+    if (shape != 0 && shape != 1) return fail(TRIMUL_ERR_INVALID_ARG, "shape must be 0 or 1; got %d", shape);
+    hipError_t e = trimul::launch_peak_mfma(seed, blocks, iters, shape, sink, stream);
     if (e != hipSuccess) return hip_fail("MFMA peak kernel launch", e);
     return ok();
 }

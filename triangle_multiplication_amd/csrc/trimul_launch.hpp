@@ -125,7 +125,7 @@ hipError_t launch_output(const Params& p, const void* z, const OutputSrc& o, int
 
 // Measured ceilings (not part of the forward pass): an MFMA-only loop and
 // plain 16-byte streams with `reads` sources and `writes` destinations.
-hipError_t launch_peak_mfma(const void* seed, int blocks, int iters, float* sink, hipStream_t s);
+hipError_t launch_peak_mfma(const void* seed, int blocks, int iters, int shape, float* sink, hipStream_t s);
 hipError_t launch_peak_stream(const void* s0, const void* s1, void* d0, void* d1, size_t n16, int reads,
                               int writes, int nontemporal, hipStream_t s);
 
