@@ -212,12 +212,14 @@ __global__ __launch_bounds__(256) void k1_project(
 //
 // With mu and rstd = 1 / sqrt(var + eps) of a z row, every projection output
 // is  W (gamma (z - mu) rstd + beta) = W' x + T  with x = (z - mu) rstd, W' the
-// weights with gamma folded in (bf16) and T = W beta (computed at create time,
-// split into bf16 high and low parts in the correction rows).  Statistics take
-// one pass with v_dot2_f32_bf16 over the raw bf16 z held in registers; z is
-// then normalised in place (x rounded to bf16), and the MFMA multiplies W'
-// with it.  Epilogue per output: a = m (acc_p + T_p) / (1 + 2^(-log2(e)
-// (acc_g + T_g))).
+// weights with gamma folded in (bf16) and T = W beta (computed at create time
+// in fp64, kept as the fp32 start vector (T, T, T, T) of each row).  For gate
+// rows W' and T also carry the factor -log2(e).  Statistics take one pass
+// with v_dot2_f32_bf16 over the raw bf16 z held in registers; z is then
+// normalised in place (x rounded to bf16), and the MFMA multiplies W' with
+// it, each accumulator starting at its row's T.  A stage ends with
+// acc_p = p and acc_g = -log2(e) g, so the epilogue per output is
+// a = m acc_p / (1 + 2^acc_g) (no m without a mask).
 //
 // A workgroup is 4 waves of 64 pairs; a wave's pairs are two adjacent rows of
 // the K-blocked a and b times one 32-wide k block, so each channel's 64 results
@@ -237,7 +239,7 @@ struct Cfg {
     static constexpr int KG = D / 32;
     static constexpr int STAGE = 32 * D * 2;                  // bytes per weight stage
     static constexpr int DPW = STAGE / 1024 / NWV;             // DMA instructions per wave per stage
-    static constexpr int EXT = 4 * CMAX * 16;                  // correction rows
+    static constexpr int EXT = 4 * CMAX * 16;                  // accumulator start vectors
     static constexpr int SC = NWV * RB * 16 * 4;               // per-pair mask values
     static constexpr int OT = NWV * 16 * ROWS * 2;             // per-wave output tiles
     static constexpr int LDS = NSW * STAGE + EXT + SC + OT;
@@ -330,8 +332,8 @@ __global__ __launch_bounds__(256, 2) void k1_project_fold(
 
     // Prologue loads, all in flight together: the raw z rows (MFMA A operand:
     // block rb, K-group kg -> chunk kg*4 + g4 of pair rb*16 + l16) and the mask
-    // into registers, then the correction rows and the first three weight
-    // stages into LDS by DMA.  Lanes of pairs that do not exist read pair 0
+    // into registers, then the accumulator start vectors and the first three
+    // weight stages into LDS by DMA.  Lanes of pairs that do not exist read pair 0
     // and are zeroed afterwards, so no load sits behind a branch.
     u32x4 zf[RB][KG];
     const u32x4 zero = {0u, 0u, 0u, 0u};
@@ -403,7 +405,7 @@ __global__ __launch_bounds__(256, 2) void k1_project_fold(
         if (MK && g4 == 0) sc[(wave * RB + rb) * 16 + l16] = mval[rb];
     }
     // Stage 0 landed (at most the DMA of stages 1 and 2 may be outstanding),
-    // then publish it, the correction rows and the mask values.
+    // then publish it, the start vectors and the mask values.
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lds0(2 * DPW));
     barrier();
 
