@@ -238,6 +238,20 @@ def test_lean_workspace_full_size_bitwise(tb):
     assert torch.equal(out, ref)
 
 
+@pytest.mark.parametrize("N,tile", [(384, 128), (200, 128), (512, 256), (640, 256), (1288, 256)])
+@pytest.mark.parametrize("masked", [False, True])
+def test_default_plan_by_shape(tb, N, tile, masked, monkeypatch):
+    """Shapes nothing was recorded for: 128-row tiles in XCD bands where
+    256-row tiles would be mostly padding (N <= 512, not a multiple of 256);
+    else 256-row tiles, walked in XCD bands unmasked and per-round XCD blocks
+    masked."""
+    monkeypatch.setenv("TRIMUL_PLAN_CACHE", "0")
+    layer = tb.TriMul(inputs.make_weights(128, 128, "bf16"), "bf16")
+    order = 1 if masked and tile == 256 else 0
+    assert tb.trimul_internal_get_plan(layer.h, 1, N, "outgoing", masked) == (0, order, 8, tile)
+    layer.close()
+
+
 def test_tune_records_a_plan_and_the_cache_reloads_it(tb, tmp_path):
     B, N, D = 1, 1288, 128
     direction = "incoming"

@@ -49,7 +49,10 @@ std::vector<Plan> candidate_plans()
 Plan default_plan(const PlanKey& k)
 {
     Plan p;
-    if (k.masked) p.k2_order = 1;
+    if (k.N <= 512 && k.N % 256 != 0)
+        p.k2_tile = 128;          // 128-row tiles walk the plain order, masked or not
+    else if (k.masked)
+        p.k2_order = 1;
     return p;
 }
 

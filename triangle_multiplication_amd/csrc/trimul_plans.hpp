@@ -41,7 +41,11 @@ std::vector<Plan> candidate_plans();
 // The plan of a call shape nothing was recorded for: 256-row tiles in groups
 // of 8 row panels; XCD bands (order 0) unmasked, per-round XCD blocks (order
 // 1) masked, where the live-first tile lists keep all XCDs on the same
-// channels (masked N = 8192, D = C = 128: 93.7 against 96.5 ms).
+// channels (masked N = 8192, D = C = 128: 93.7 against 96.5 ms).  At N <= 512
+// that is not a multiple of 256, 128-row tiles in XCD bands: 256-row tiles
+// would be mostly padding (N = 384: 0.028 against 0.032 ms unmasked, 0.0335
+// against 0.0345 ms masked); where N fills 256-row tiles, they are faster
+// (N = 512, D = C = 256: 0.091 against 0.121 ms).
 Plan default_plan(const PlanKey& k);
 
 // Whether a plan is one of the candidates (plans read from a file or set by a
