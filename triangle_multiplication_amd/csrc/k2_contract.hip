@@ -517,17 +517,22 @@ __global__ __launch_bounds__(512) void k2_contract_ppp(K2PArgs args)
 // [32 lo, 32 hi) is zero for all rows of tile t; (0, 0) if no key is live.
 // A mask value counts as live unless it compares equal to zero (-0 is zero,
 // NaN is live, so a NaN still reaches the output).
-// One 256-thread workgroup per (tile, batch element) reads the tile's mask
+// One 1024-thread workgroup per (tile, batch element) reads the tile's mask
 // rows (outgoing) or columns (incoming) once, in 16-byte chunks, eight loads
-// in flight per thread.
+// in flight per thread (128 KB per workgroup; with 256 threads the scan took
+// 13-16 us at N = 384, where each of the two workgroups waited on six rounds
+// of loads).
 // ---------------------------------------------------------------------------
 template <typename T>
 __device__ inline bool mask_live(T v) { return v != (T)0; }
 
+constexpr int K0_THREADS = 1024;
+
 template <typename T>
-__global__ __launch_bounds__(256) void k0_mask_ranges(const T* __restrict__ mask, int N, int incoming,
-                                                      int* __restrict__ ranges, int* __restrict__ hdr)
+__global__ __launch_bounds__(K0_THREADS) void k0_mask_ranges(const T* __restrict__ mask, int N, int incoming,
+                                                             int* __restrict__ ranges, int* __restrict__ hdr)
 {
+    constexpr int NT = K0_THREADS;
     if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 4) hdr[threadIdx.x] = 0;
     constexpr int CE = 16 / (int)sizeof(T);        // elements per 16-byte chunk
     const int t = blockIdx.x, b = blockIdx.y, tiles = gridDim.x;
@@ -543,16 +548,16 @@ __global__ __launch_bounds__(256) void k0_mask_ranges(const T* __restrict__ mask
         // idx = r * nch + c of the tile's rows.
         const int nch = N / CE, total = rows * nch;
         const T* tile0 = m + (size_t)r0 * N;
-        for (int base = tid; base < total; base += 256 * U) {
+        for (int base = tid; base < total; base += NT * U) {
             u32x4 v[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int idx = min(base + u * 256, total - 1);
+                const int idx = min(base + u * NT, total - 1);
                 v[u] = ld16(tile0 + (size_t)(idx / nch) * N + (size_t)(idx % nch) * CE);
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int idx = base + u * 256;
+                const int idx = base + u * NT;
                 if (idx >= total) break;
                 const int key0 = (idx % nch) * CE;
                 const T* e = reinterpret_cast<const T*>(&v[u]);
@@ -568,7 +573,7 @@ __global__ __launch_bounds__(256) void k0_mask_ranges(const T* __restrict__ mask
         // Columns r0 .. r0 + rows - 1 of every mask row k: key k is live if any
         // of them is.
         const int cpr = rows / CE;                  // chunks per mask row (1 .. 64)
-        const int rpi = 256 / cpr;                  // mask rows per pass
+        const int rpi = NT / cpr;                   // mask rows per pass
         const int c = tid % cpr, k0 = tid / cpr;
         if (k0 < rpi)
             for (int kb = k0; kb < N; kb += rpi * U) {
@@ -598,12 +603,16 @@ __global__ __launch_bounds__(256) void k0_mask_ranges(const T* __restrict__ mask
         kmin = min(kmin, __shfl_xor(kmin, off));
         kmax = max(kmax, __shfl_xor(kmax, off));
     }
-    __shared__ int smin[4], smax[4];
+    __shared__ int smin[NT / 64], smax[NT / 64];
     if ((tid & 63) == 0) { smin[tid >> 6] = kmin; smax[tid >> 6] = kmax; }
     __syncthreads();
     if (tid == 0) {
-        kmin = min(min(smin[0], smin[1]), min(smin[2], smin[3]));
-        kmax = max(max(smax[0], smax[1]), max(smax[2], smax[3]));
+        for (int w = 1; w < NT / 64; ++w) {
+            smin[0] = min(smin[0], smin[w]);
+            smax[0] = max(smax[0], smax[w]);
+        }
+        kmin = smin[0];
+        kmax = smax[0];
         int* dst = ranges + ((size_t)b * tiles + t) * 2;
         dst[0] = kmax < 0 ? 0 : kmin / K2_KSTEP;
         dst[1] = kmax < 0 ? 0 : kmax / K2_KSTEP + 1;
@@ -617,10 +626,11 @@ hipError_t launch_mask_ranges(const Params& p, const void* mask, int B, int N, i
     int* hdr = table + 2 * (size_t)B * tiles;
     dim3 grid((unsigned)tiles, (unsigned)B);
     if (p.dtype == DType::BF16)
-        hipLaunchKernelGGL(k0_mask_ranges<bf16>, grid, dim3(256), 0, s, (const bf16*)mask, N, incoming, table, hdr);
-    else
-        hipLaunchKernelGGL(k0_mask_ranges<float>, grid, dim3(256), 0, s, (const float*)mask, N, incoming, table,
+        hipLaunchKernelGGL(k0_mask_ranges<bf16>, grid, dim3(K0_THREADS), 0, s, (const bf16*)mask, N, incoming, table,
                            hdr);
+    else
+        hipLaunchKernelGGL(k0_mask_ranges<float>, grid, dim3(K0_THREADS), 0, s, (const float*)mask, N, incoming,
+                           table, hdr);
     return hipGetLastError();
 }
 
