@@ -1,7 +1,8 @@
 """The measured-ceiling kernels the benchmark reports against
 (trimul_internal_peak_stream / _mfma): the streams move exactly the bytes
-their mode defines, over sizes that end inside the four-chunk unrolled loop,
-and the MFMA-only loop accumulates linearly in its iteration count."""
+their mode defines, over sizes that end inside a workgroup (one 16-byte chunk
+per thread, 256 threads) and at its edge, and the MFMA-only loop accumulates
+linearly in its iteration count."""
 import pytest
 import torch
 
