@@ -358,23 +358,34 @@ __global__ __launch_bounds__(k3f::waves_for(D) * 64) void k3_output_fold(
     const int l16 = lane & 15, g4 = lane >> 4;
     const size_t NN = (size_t)N * N;
     const int G = gridDim.x, g = blockIdx.x;
-    // This workgroup's tiles: one contiguous range of 64-pair runs, each as two
-    // 32-pair halves, so every workgroup streams its own contiguous stretch of
-    // z, out and each channel of o (measured against walking runs g, g + G,
-    // ...: -1 % at D = 256, -7 % at D = 128 with two workgroups per CU).  The
-    // walk starts at a position rotated by 97 g runs within the range and
-    // wraps: with aligned starts, the lines the workgroups of an XCD read at
-    // the same time sat at power-of-two distances and evicted each other from
-    // L2, so a third of o's lines were fetched twice (the next tile reads the
-    // second half of each).
-    const long long s_begin = (long long)g * n_super / G, s_end = (long long)(g + 1) * n_super / G;
-    const int n_runs = (int)(s_end - s_begin);
+    // This workgroup's tiles: 64-pair runs, each as two 32-pair halves back to
+    // back (the second half of each 128-byte line of o is then an L2 hit).
+    // At D = 256 the workgroups walk runs g, g + G, ..., all on one moving
+    // window (1.5-3 % faster there than the contiguous ranges below).  At D =
+    // 128 each workgroup walks one contiguous range of runs, so it streams its
+    // own stretch of z, out and each channel of o (6-9 % faster than the
+    // moving window with two workgroups per CU, the same with one); the walk
+    // starts at a position rotated by 97 g runs within the range and wraps:
+    // with aligned starts, the lines the workgroups of an XCD read at the same
+    // time sat at power-of-two distances and evicted each other from L2, so a
+    // third of o's lines were fetched twice.  G <= n_super, so every
+    // workgroup has at least one run.
+    constexpr bool WINDOW = D >= 256;
+    const long long s_begin = WINDOW ? g : (long long)g * n_super / G;
+    const int n_runs = WINDOW ? (int)((n_super - g + G - 1) / G)
+                              : (int)((long long)(g + 1) * n_super / G - s_begin);
     const int n_tiles = 2 * n_runs;
-    const int rot = n_runs > 0 ? (int)(((long long)g * 97) % n_runs) : 0;
+    const int rot = (WINDOW || n_runs == 0) ? 0 : (int)(((long long)g * 97) % n_runs);
     auto tile_p0 = [&](int it) -> size_t {
-        int r = (it >> 1) + rot;
-        if (r >= n_runs) r -= n_runs;
-        return it < n_tiles ? ((size_t)(s_begin + r) * 64 + (it & 1) * 32) : 0;
+        long long run;
+        if constexpr (WINDOW) {
+            run = s_begin + (long long)(it >> 1) * G;
+        } else {
+            int r = (it >> 1) + rot;
+            if (r >= n_runs) r -= n_runs;
+            run = s_begin + r;
+        }
+        return it < n_tiles ? ((size_t)run * 64 + (it & 1) * 32) : 0;
     };
 
     // Weight rows of this wave (MFMA A operand: lane = row l16 of the block,
