@@ -158,6 +158,26 @@ def test_output_stage(tb, dtype, B, N, D, C):
     assert rel_err(out.float().cpu().numpy(), ref) <= TOL[dtype]
 
 
+@pytest.mark.parametrize("N,D,C", [(200, 256, 128), (328, 256, 256), (456, 128, 128), (264, 128, 256)])
+def test_output_stage_multi_run(tb, N, D, C):
+    """Sizes at which every workgroup of the folded output kernel walks several
+    64-pair runs and the run count does not divide by the workgroup count:
+    the strided walk over one moving window (D = 256) and the rotated walk of
+    contiguous ranges (D = 128) must each cover every pair exactly once."""
+    B = 1
+    say("output stage multi-run", N, D, C)
+    w = inputs.make_weights(D, C, "bf16", random_ln=True)
+    z = inputs.make_z(B, N, D, "bf16")
+    g = torch.Generator("cpu").manual_seed(11)
+    o = (torch.randn((B, C, N, N), generator=g) * 2.0 - 0.3).to(torch.bfloat16)
+    ref = oracle.output_stage(z.float().numpy(), o.float().permute(0, 2, 3, 1).numpy(), w)
+    layer = _layer(tb, w, "bf16")
+    out = layer.output(z.cuda(), o.cuda())
+    err = rel_err(out.float().cpu().numpy(), ref)
+    say("  err", err)
+    assert err <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("D,C", [(128, 128), (256, 256), (256, 128), (128, 256), (128, 64), (128, 192)])
 @pytest.mark.parametrize("mean", [20.0, -40.0])
 def test_output_stage_shifted_o_mean(tb, D, C, mean):
