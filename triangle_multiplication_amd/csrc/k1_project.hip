@@ -429,12 +429,18 @@ __global__ __launch_bounds__(256, 2) void k1_project_fold(
     constexpr int HB = RB / 2;
     constexpr int NOUT = HB * 4;   // epilogue outputs per lane per half
     // Mask values of this lane's four output pairs in every block (they do not
-    // change from stage to stage).
-    f32x4 mrr[RB];
+    // change from stage to stage), two bf16 per register: the mask is bf16, so
+    // the packing is exact, and each value is unpacked to fp32 by one shift or
+    // mask where it is used.  Held as fp32 they cost 8 more registers, which
+    // at D = 128 is one workgroup per CU fewer and at D = 256 spills.
+    u32x2 mrr[RB];
     if constexpr (MK) {
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-            mrr[rb] = *reinterpret_cast<const f32x4*>(sc + (wave * RB + rb) * 16 + 4 * g4);
+        for (int rb = 0; rb < RB; ++rb) {
+            const f32x4 mv = *reinterpret_cast<const f32x4*>(sc + (wave * RB + rb) * 16 + 4 * g4);
+            mrr[rb] = u32x2{(__float_as_uint(mv[0]) >> 16) | (__float_as_uint(mv[1]) & 0xffff0000u),
+                            (__float_as_uint(mv[2]) >> 16) | (__float_as_uint(mv[3]) & 0xffff0000u)};
+        }
     }
     // Start vectors of this lane's output channel (column l16 of stage q's 16 p
     // rows and 16 g rows): every accumulator of a stage starts at its channel's
@@ -453,7 +459,11 @@ __global__ __launch_bounds__(256, 2) void k1_project_fold(
         constexpr int HP = decltype(hpc)::value;
         const int j = k / 4, e = k % 4, rb = HP * HB + j;
         const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(gp[j][e]));
-        if constexpr (MK) ov[j][e] = mrr[rb][e] * pp[j][e] * sg;
+        if constexpr (MK) {
+            const uint32_t w = mrr[rb][e >> 1];
+            const float mv = __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+            ov[j][e] = mv * pp[j][e] * sg;
+        }
         else ov[j][e] = pp[j][e] * sg;
         if (e == 3) {
             bf16x4 h;
