@@ -175,7 +175,7 @@ def test_every_plan_gives_the_same_bits(tb, direction, masked):
     z = inputs.make_z(B, N, D, "bf16").cuda()
     mask = inputs.pair_mask(inputs.token_mask_tail(N), B, "bf16").cuda() if masked else None
     plans = tb.plan_candidates()
-    default = (0, 1 if masked else 0, 8, 256)
+    default = (0, 1, 8, 256)
     assert tb.trimul_internal_get_plan(layer.h, B, N, direction, masked) == default
     assert default in plans
     ref = layer.forward(z, mask, direction)
@@ -243,11 +243,10 @@ def test_lean_workspace_full_size_bitwise(tb):
 def test_default_plan_by_shape(tb, N, tile, masked, monkeypatch):
     """Shapes nothing was recorded for: 128-row tiles in XCD bands where
     256-row tiles would be mostly padding (N <= 512, not a multiple of 256);
-    else 256-row tiles, walked in XCD bands unmasked and per-round XCD blocks
-    masked."""
+    else 256-row tiles in per-round XCD blocks, masked or not."""
     monkeypatch.setenv("TRIMUL_PLAN_CACHE", "0")
     layer = tb.TriMul(inputs.make_weights(128, 128, "bf16"), "bf16")
-    order = 1 if masked and tile == 256 else 0
+    order = 1 if tile == 256 else 0
     assert tb.trimul_internal_get_plan(layer.h, 1, N, "outgoing", masked) == (0, order, 8, tile)
     layer.close()
 

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 def test_candidates_include_the_default_first():
     c = tb.plan_candidates()
-    assert c[0] == (0, 0, 8, 256)
+    assert c[0] == (0, 1, 8, 256)
     assert len(c) == len(set(c)) >= 2
     assert {p[1] for p in c} == {0, 1} and {p[2] for p in c} == {4, 8, 16} and {p[3] for p in c} == {256, 128}
 

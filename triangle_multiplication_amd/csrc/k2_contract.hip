@@ -189,6 +189,8 @@ __device__ inline int slot_off(int row, int chunk)
 // in its L2 (gm = 8 measured best against 1, 2, 4 and 16 at N = 4096 with
 // order 0).
 //
+// k2_contract_ppp below runs one K-step per phase (the 128-row-tile plans);
+// k2_contract_pp2 after it runs two (256-row tiles) on the same scheme.
 // 8 waves in a 2 x 4 grid, each owning a 128 x 64 block of the tile (8 x 4
 // MFMA tiles, 128 accumulators per lane); the two waves that share a SIMD
 // (wave w and w + 4) run half a step apart ("ping-pong").  Each wave
@@ -508,6 +510,276 @@ __global__ __launch_bounds__(512) void k2_contract_ppp(K2PArgs args)
 }
 
 // ---------------------------------------------------------------------------
+// Two K-steps per phase (256-row tiles).  The same tiles, walk, key ranges,
+// fragment layout and MFMA order per output as k2_contract_ppp<NSP, 256, MK>
+// (so the same bits), but each memory phase reads the fragments of two steps
+// and each compute phase runs 64 MFMAs, so the per-phase cost of the barrier,
+// the waits and the LDS latency is paid once per two steps.  A copy of the
+// one-step kernel that ran every MFMA twice per phase reached the rate of an
+// MFMA-only loop, which is what this form aims at.
+//
+// Ring: 5 slots of one step (160 KB), step k in slot k % 5.  Super-step u is
+// steps 2u and 2u + 1; phase p: group 0 runs M_{p/2} (p even) or C_{(p-1)/2};
+// group 1 the same one phase later.  Each group loads whole steps: group 0 the
+// odd steps (step 2u + 3 in M_u), group 1 the even ones (step 2u + 4 in M_u),
+// each wave eight 1 KB DMA instructions (rows 64 w' .. + 63 of both operands,
+// w' = wave % 4).  Invariants:
+//  - step 2u + 3 overwrites step 2u - 2 and step 2u + 4 step 2u - 1 (super-step
+//    u - 1), first in phase 2u, after the barrier ending phase 2u - 1 where
+//    group 1 finished reading them (memory phases end with lgkmcnt(0));
+//  - super-step v is read from phase 2v on; its odd step was loaded by group 0
+//    in phase 2v - 2 and its even step by group 1 in phase 2v - 3.  Group 0
+//    waits for all its loads at the end of each compute phase (phase 2v - 1),
+//    group 1 for all but its newest step at the end of each phase, so both
+//    steps have landed for everyone when phase 2v starts.
+// A tile's step count is rounded up to even; the extra step reads zeros (its
+// DMA is pushed out of the buffer's range), which adds exact zeros.
+// ---------------------------------------------------------------------------
+template <bool MK>
+__global__ __launch_bounds__(512) void k2_contract_pp2(K2PArgs args)
+{
+    using namespace k2big;
+    constexpr int NSP = 5, TB = 256;
+    constexpr int NW = 8;
+    constexpr int RG = TB / 16;                     // 16-row groups of the tile
+    constexpr int WM = TB / 2, WN = TB / 4;         // a wave's block of the tile
+    constexpr int MB = WM / 16, NB = WN / 16;       // its 16 x 16 MFMA blocks
+    constexpr int DPW = 8;                          // DMA instructions per loading wave per step
+    static_assert(NB % 2 == 0 && RG % 2 == 0 && OPB == 16 * 1024, "paired column blocks, 16 KB operands");
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[NSP * STB];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 2, wn = wave & 3;        // group = wm
+    const int N = args.N, total = args.total;
+    const int tiles = (N + TB - 1) / TB;
+    const int per_bc = tiles * tiles;
+    const int G = gridDim.x, g = blockIdx.x;
+    const int n_my = (total - g + G - 1) / G;       // tiles of this workgroup (g < total)
+    const int nk = (N + BK - 1) / BK;               // steps of a whole tile
+    constexpr bool use_pairs = MK;
+
+    auto logical_of = [&](unsigned vb) -> unsigned {
+        if (args.order == 0) return (vb & 7u) * ((unsigned)total >> 3) + (vb >> 3);
+        const unsigned r = vb / (unsigned)G, gg = vb - r * (unsigned)G;
+        const unsigned rem = (unsigned)total - r * (unsigned)G;
+        const unsigned R = rem < (unsigned)G ? rem : (unsigned)G;
+        return r * (unsigned)G + (gg & 7u) * (R >> 3) + (gg >> 3);
+    };
+    const unsigned nl = use_pairs ? (unsigned)args.hdr[0] : 0u;
+    const unsigned nbc_l = (unsigned)total / (unsigned)per_bc;
+    auto tile_geo = [&](int tl, size_t& bc, int& ti, int& tj) {
+        const unsigned logical = logical_of((unsigned)g + (unsigned)tl * (unsigned)G);
+        if (use_pairs) {
+            unsigned p;
+            if (logical < nbc_l * nl) {
+                bc = logical / nl;
+                p = logical % nl;
+            } else {
+                const unsigned r = logical - nbc_l * nl, nd = (unsigned)per_bc - nl;
+                bc = r / nd;
+                p = nl + r % nd;
+            }
+            const unsigned e = args.pairs[((size_t)args.bc0 + bc) / (size_t)args.C * per_bc + p];
+            ti = (int)(e & 0xffffu);
+            tj = (int)(e >> 16);
+            return;
+        }
+        bc = logical / per_bc;
+        const int t = (int)(logical % per_bc);
+        const int GM = args.gm;
+        const int first_i = (t / (GM * tiles)) * GM;
+        const int gm = min(GM, tiles - first_i);
+        ti = first_i + (t % (GM * tiles)) % gm;
+        tj = (t % (GM * tiles)) / gm;
+    };
+    const int t256 = (N + BM - 1) / BM;
+    // K-steps of tile (bc, ti, tj): [klo, klo + kn), kn >= 1 (see the one-step kernel).
+    auto krange = [&](size_t bc, int ti, int tj, int& klo, int& kn, bool& live) {
+        if constexpr (!MK) {
+            klo = 0;
+            kn = nk;
+            live = true;
+        } else {
+            const int b = (int)(((size_t)args.bc0 + bc) / (size_t)args.C);
+            const int* r = args.ranges + (size_t)b * t256 * 2;
+            const int lo = __builtin_amdgcn_readfirstlane(max(r[2 * ti], r[2 * tj]));
+            const int hi = __builtin_amdgcn_readfirstlane(min(r[2 * ti + 1], r[2 * tj + 1]));
+            live = lo < hi;
+            klo = live ? lo : 0;
+            kn = live ? hi - lo : 1;
+        }
+    };
+
+    // DMA lanes: lane l reads row dr, chunk dc of a 16-row kilobyte (the slot
+    // swizzle is applied by choosing which lane reads which chunk).  Loading
+    // wave w' fills kilobytes 4 w' + i (i = 0..3) of both operands: A rows
+    // 16 j + dr of kilobyte j; B rows permuted within each 32-row group (slot
+    // row 16 h + r holds tile row 8 (r / 4) + 4 h + r % 4) as in the one-step
+    // kernel, so a lane stores eight consecutive j of one i.
+    const size_t aslab = ab_slab_elems(DType::BF16, N);
+    const unsigned nrec = (unsigned)(aslab * sizeof(bf16));
+    const int dpos = (lane & 7) ^ (lane >> 3);
+    const int dr = 2 * (lane >> 3) + (dpos >> 2), dc = dpos & 3;
+    const unsigned kstride = (unsigned)N * ROWB;    // bytes per K-block
+    const int wq = wave & 3;                        // w'
+    const unsigned lane_off = (unsigned)(64 * wq + dr) * ROWB + dc * 16u;
+    const unsigned lane_off_b = (unsigned)(64 * wq + 8 * (dr >> 2) + (dr & 3)) * ROWB + dc * 16u;
+
+    // DMA cursor over the workgroup's step sequence (tiles back to back, each
+    // padded to an even step count): step ikk of tile itl, first key ik0,
+    // byte offset ikb, ring slot isl.
+    int itl = 0, ikk = 0, ikn = 1, ikn2 = 2, ik0 = 0, isl = 0;
+    unsigned ikb = 0;
+    __amdgpu_buffer_rsrc_t ra, rb;
+    unsigned oa_t = 0, ob_t = 0;
+    bool ilive = true;
+    auto set_tile = [&]() {
+        const bool have = itl < n_my;
+        size_t bc; int ti, tj, iklo;
+        tile_geo(have ? itl : 0, bc, ti, tj);
+        bool klive;
+        krange(bc, ti, tj, iklo, ikn, klive);
+        ikn2 = (ikn + 1) & ~1;
+        ilive = have && klive;
+        const size_t sb = (size_t)args.bc0 + bc;
+        ra = __builtin_amdgcn_make_buffer_rsrc((void*)(args.A + sb * aslab), 0, nrec, 0x00020000);
+        rb = __builtin_amdgcn_make_buffer_rsrc((void*)(args.Bm + sb * aslab), 0, nrec, 0x00020000);
+        oa_t = lane_off + (unsigned)(ti * TB) * ROWB;
+        ob_t = lane_off_b + (unsigned)(tj * TB) * ROWB;
+        ik0 = iklo * BK;
+        ikb = (unsigned)iklo * kstride;
+    };
+    set_tile();
+    auto advance = [&]() {
+        ik0 += BK;
+        ikb += kstride;
+        if (++isl == NSP) isl = 0;
+        if (++ikk == ikn2) { ikk = 0; ++itl; set_tile(); }
+    };
+    auto issue = [&]() {                            // this wave's share of the cursor's step
+        unsigned char* st = smem + isl * STB + wq * 4 * 1024;
+        const unsigned kpen = (ilive && ikk < ikn && ik0 + dc * 8 < N) ? 0u : 0x80000000u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, TRIMUL_LDS_PTR(st + i * 1024), 16,
+                                                     (oa_t + i * 16u * ROWB + ikb) | kpen, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rb, TRIMUL_LDS_PTR(st + OPB + i * 1024), 16,
+                (ob_t + (32u * (i >> 1) + 4u * (i & 1)) * ROWB + ikb) | kpen, 0, 0, 0);
+        }
+    };
+
+    const int rchunk = lane >> 4;
+    const int fa_base = slot_off(wm * WM + (lane & 15), rchunk);
+    const int fb_base = OPB + slot_off(wn * WN + (lane & 15), rchunk);
+
+    f32x4 acc[MB][NB];
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+        for (int n = 0; n < NB; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    u32x4 fa[2][MB], fb[2][NB];
+    auto barrier = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // Prologue: group 1 loads steps 0 and 2, group 0 step 1; then the cursor
+    // of each group stands on its first step of the loop (3 or 4).
+    if (wm == 1) {
+        issue(); advance(); advance();
+        issue(); advance(); advance();
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(DPW));    // step 0 landed (own share)
+    } else {
+        advance();
+        issue(); advance(); advance();
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));      // step 1 landed (own share)
+    }
+    barrier();                                          // steps 0 and 1 landed for everyone
+    if (wm == 1) barrier();                             // group 1 starts one phase late
+
+    int kin = 0;                                        // super-step within the current tile
+    int tl = 0;
+    int nk2;                                            // super-steps of tile tl
+    {
+        size_t bc; int ti, tj, klo, kn; bool lv;
+        tile_geo(0, bc, ti, tj);
+        krange(bc, ti, tj, klo, kn, lv);
+        nk2 = (kn + 1) >> 1;
+    }
+    int rsl = 0;                                        // ring slot of the current super-step's first step
+    for (;;) {
+        // M_u: fragments of steps 2u and 2u + 1, then this group's next step.
+        const unsigned char* st0 = smem + rsl * STB;
+        if (++rsl == NSP) rsl = 0;
+        const unsigned char* st1 = smem + rsl * STB;
+        if (++rsl == NSP) rsl = 0;
+#pragma unroll
+        for (int m = 0; m < MB; ++m) fa[0][m] = *reinterpret_cast<const u32x4*>(st0 + fa_base + m * 1024);
+#pragma unroll
+        for (int n = 0; n < NB; ++n) fb[0][n] = *reinterpret_cast<const u32x4*>(st0 + fb_base + n * 1024);
+#pragma unroll
+        for (int m = 0; m < MB; ++m) fa[1][m] = *reinterpret_cast<const u32x4*>(st1 + fa_base + m * 1024);
+#pragma unroll
+        for (int n = 0; n < NB; ++n) fb[1][n] = *reinterpret_cast<const u32x4*>(st1 + fb_base + n * 1024);
+        issue();
+        advance();
+        advance();
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lds0(DPW));   // all but the step just issued
+        barrier();
+        // C_u.  Operands swapped (b rows as the MFMA's A): each lane's four
+        // results are four consecutive j of one i.
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int m = 0; m < MB; ++m)
+#pragma unroll
+                for (int n = 0; n < NB; ++n) acc[m][n] = Elem<bf16>::mma(fb[h][n], fa[h][m], acc[m][n]);
+        if (wm == 0) __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));     // its step of the next super-step
+        else __builtin_amdgcn_s_waitcnt(waitcnt_vm(DPW));
+        barrier();
+        if (++kin == nk2) {
+            // Tile tl complete: store this wave's block and start the next.
+            size_t bc; int ti, tj;
+            tile_geo(tl, bc, ti, tj);
+            const int i0 = ti * TB, j0 = tj * TB;
+            bf16* Ob = args.O + bc * args.o_stride;
+#pragma unroll
+            for (int m = 0; m < MB; ++m) {
+                const int i = i0 + wm * WM + m * 16 + (lane & 15);
+#pragma unroll
+                for (int p = 0; p < NB / 2; ++p) {
+                    // j .. j + 7 (8 divides N, so all or none exist)
+                    const int j = j0 + wn * WN + 32 * p + 8 * (lane >> 4);
+                    bf16x8 h;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        h[e] = (bf16)acc[m][2 * p][e];
+                        h[4 + e] = (bf16)acc[m][2 * p + 1][e];
+                    }
+                    if (i < N && j < N) *reinterpret_cast<bf16x8*>(Ob + (size_t)i * N + j) = h;
+                    acc[m][2 * p] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    acc[m][2 * p + 1] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+            kin = 0;
+            if (++tl == n_my) break;
+            size_t nbc; int nti, ntj, klo, kn; bool lv;
+            tile_geo(tl, nbc, nti, ntj);
+            krange(nbc, nti, ntj, klo, kn, lv);
+            nk2 = (kn + 1) >> 1;
+        }
+    }
+    if (wm == 0) barrier();                             // balance group 1's extra barrier
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));          // no DMA may outlive the workgroup
+}
+
+// ---------------------------------------------------------------------------
 // Live key ranges of the contraction's row tiles, read from the pair mask.
 //
 // Row r, key k of both operands is scaled by M[r][k] = mask[b][r][k]
@@ -722,9 +994,11 @@ static hipError_t launch_k2(const void* a, const void* b, int N, const ContractJ
 hipError_t launch_contract(const Params& p, const Plan& plan, const void* a_cm, const void* b_cm,
                            int B, int N, const ContractJob& job, hipStream_t s)
 {
-    // bf16: the persistent kernel with the plan's tile side (256 by default;
-    // 128 wastes less on ragged edges at small N); ragged tiles read zeros or
-    // rows whose outputs are never stored.
+    // bf16: the persistent kernels with the plan's tile side: 256-row tiles
+    // (default) run two K-steps per phase (k2_contract_pp2), 128-row tiles,
+    // which waste less on ragged edges at small N, one 64-key step per phase
+    // (k2_contract_ppp; its 160 KB would not hold two of their steps and the
+    // ring); ragged tiles read zeros or rows whose outputs are never stored.
     if (p.dtype == DType::BF16) {
         const int TB = plan.k2_tile == 128 ? 128 : 256;
         const int tiles = (N + TB - 1) / TB;
@@ -754,8 +1028,8 @@ hipError_t launch_contract(const Params& p, const Plan& plan, const void* a_cm, 
             if (mk) hipLaunchKernelGGL((k2_contract_ppp<4, 128, true>), dim3((unsigned)pg), dim3(512), 0, s, a);
             else hipLaunchKernelGGL((k2_contract_ppp<4, 128, false>), dim3((unsigned)pg), dim3(512), 0, s, a);
         } else {
-            if (mk) hipLaunchKernelGGL((k2_contract_ppp<4, 256, true>), dim3((unsigned)pg), dim3(512), 0, s, a);
-            else hipLaunchKernelGGL((k2_contract_ppp<4, 256, false>), dim3((unsigned)pg), dim3(512), 0, s, a);
+            if (mk) hipLaunchKernelGGL((k2_contract_pp2<true>), dim3((unsigned)pg), dim3(512), 0, s, a);
+            else hipLaunchKernelGGL((k2_contract_pp2<false>), dim3((unsigned)pg), dim3(512), 0, s, a);
         }
         return hipGetLastError();
     }

@@ -24,7 +24,7 @@ std::vector<Plan> k2_choices()
 {
     std::vector<Plan> v;
     for (int tile : {256, 128})
-        for (int order : {0, 1})
+        for (int order : {1, 0})
             for (int gm : {8, 4, 16}) {
                 Plan p;
                 p.k2_order = order;
@@ -51,7 +51,7 @@ Plan default_plan(const PlanKey& k)
     Plan p;
     if (k.N <= 512 && k.N % 256 != 0)
         p.k2_tile = 128;          // 128-row tiles walk the plain order, masked or not
-    else if (k.masked)
+    else
         p.k2_order = 1;
     return p;
 }

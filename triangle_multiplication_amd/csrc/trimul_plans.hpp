@@ -35,17 +35,20 @@ struct PlanEntry {
 // (each kernel is timed on its own, and the fastest of each kept).
 std::vector<int> k1_variants();
 std::vector<Plan> k2_choices();
-// Every combination, the unmasked default first.
+// Every combination, the default for 256-row tiles first.
 std::vector<Plan> candidate_plans();
 
 // The plan of a call shape nothing was recorded for: 256-row tiles in groups
-// of 8 row panels; XCD bands (order 0) unmasked, per-round XCD blocks (order
-// 1) masked, where the live-first tile lists keep all XCDs on the same
-// channels (masked N = 8192, D = C = 128: 93.7 against 96.5 ms).  At N <= 512
-// that is not a multiple of 256, 128-row tiles in XCD bands: 256-row tiles
-// would be mostly padding (N = 384: 0.028 against 0.032 ms unmasked, 0.0335
-// against 0.0345 ms masked); where N fills 256-row tiles, they are faster
-// (N = 512, D = C = 256: 0.091 against 0.121 ms).
+// of 8 row panels, per-round XCD blocks (order 1), which keep all XCDs on the
+// same channels (with the two-step contraction, K2 ms on one box, order 1
+// against XCD bands: 24.60 against 24.90 at N = 4096, D = C = 256; 98.6
+// against 99.9 at N = 8192, D = C = 128; 0.52 against 0.56 at B = 2, N =
+// 1024; 3.55 against 3.49 at N = 2048; masked N = 8192 with the live-first
+// tile lists: 93.7 against 96.5).  At N <= 512 that is not a multiple of 256,
+// 128-row tiles in XCD bands: 256-row tiles would be mostly padding (N = 384:
+// 0.028 against 0.032 ms unmasked, 0.0335 against 0.0345 ms masked); where N
+// fills 256-row tiles, they are faster (N = 512, D = C = 256: 0.091 against
+// 0.121 ms).
 Plan default_plan(const PlanKey& k);
 
 // Whether a plan is one of the candidates (plans read from a file or set by a
