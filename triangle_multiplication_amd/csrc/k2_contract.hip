@@ -511,8 +511,9 @@ __global__ __launch_bounds__(512) void k2_contract_ppp(K2PArgs args)
 
 // ---------------------------------------------------------------------------
 // Two K-steps per phase (256-row tiles).  The same tiles, walk, key ranges,
-// fragment layout and MFMA order per output as k2_contract_ppp<NSP, 256, MK>
-// (so the same bits), but each memory phase reads the fragments of two steps
+// fragment layout and MFMA order per output as the one-step kernel above
+// would use at 256-row tiles (so the same bits as every other plan: each
+// output sums its keys in the same MFMA sequence), but each memory phase reads the fragments of two steps
 // and each compute phase runs 64 MFMAs, so the per-phase cost of the barrier,
 // the waits and the LDS latency is paid once per two steps.  A copy of the
 // one-step kernel that ran every MFMA twice per phase reached the rate of an
